@@ -1,0 +1,197 @@
+/*
+ * pa.h -- C ABI of libpagedattn: paged KV attention for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by title and section):
+ *   [guide]  "tiny-vllm：从零构建高性能LLM推理引擎的完整指南"
+ *   [实战]   "Tiny-vLLM 实战：用 C++/CUDA 手写高性能 LLM 推理引擎"
+ *
+ * The problem, as those pages state it: the KV cache is cut into fixed-size pages
+ * taken from a preallocated pool ([实战] §内存池管理); a free-page list hands pages
+ * out on demand and takes them back when a request ends; pages may be shared by
+ * requests with a common prefix; each sequence reaches its pages through a block table
+ * ([guide] §PagedAttention); each new token's K/V is appended to the cache before it
+ * attends ([guide] §推理流程：从Prefill到Decode); attention runs with online softmax
+ * ([guide] §在线Softmax) on bf16 data with fp32 accumulation ([实战] §CUDA Kernel 优化,
+ * 数据类型精度权衡), with grouped-query heads ([guide] §Llama 3.2 1B架构拆解).
+ *
+ * Conventions for every entry point:
+ *   - Status: 0 (PA_OK) or a negative PA_ERR_* code.  Nothing aborts and nothing throws
+ *     across the ABI.  Host-checkable errors return before anything is launched.
+ *   - Device pointers are caller-owned device memory (the library never allocates or
+ *     frees device memory); they must stay valid until the work queued on `stream`
+ *     has finished.  `stream` is a hipStream_t passed as void* (NULL = null stream).
+ *     Launches are asynchronous.
+ *   - Values stored on the device (block-table entries, context lengths, cumulative
+ *     lengths) are trusted, except that every kernel clamps a sequence's length to its
+ *     block-table row (max_blocks_per_seq * block_size) and never dereferences a page
+ *     id outside [0, num_pages): a read of such a page yields NaN in that output row,
+ *     a write to it is dropped.
+ *
+ * Memory layout (bf16 = 2 bytes; the pages fix only a page's size, block_size x
+ * head_dim x num_kv_heads values, [实战] §内存池管理; the order inside is this
+ * library's choice):
+ *   k_pool  [num_pages][num_kv_heads][head_dim/8][block_size][8]   bf16
+ *   v_pool  [num_pages][num_kv_heads][head_dim][block_size]        bf16
+ *   block_tables  int32 [n_seqs][max_blocks_per_seq]: logical block b of sequence s
+ *                 lives in physical page block_tables[s*max_blocks_per_seq + b]
+ *   q, out, k_new, v_new: token-major rows [tokens][heads][head_dim] bf16
+ *   Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * One pool pair holds one layer; other layers are served by calling again with their
+ * pool pointers (one block table may serve all layers).
+ *
+ * Supported geometry: head_dim 64, block_size 16 or 32, num_q_heads = 4 * num_kv_heads
+ * (the Llama-3.2-1B shape is 32 query heads over 8 KV heads).  Anything else returns
+ * PA_ERR_UNSUPPORTED.
+ */
+#ifndef PAGEDATTN_PA_H
+#define PAGEDATTN_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent sizes, bad page id */
+  PA_ERR_OUT_OF_PAGES = -2, /* pool cannot satisfy an allocation */
+  PA_ERR_UNSUPPORTED = -3,  /* geometry outside the supported set */
+  PA_ERR_WORKSPACE = -4,    /* split-K workspace missing or too small */
+  PA_ERR_HIP = -5           /* a HIP runtime call or launch failed; see pa_last_hip_error */
+};
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* pa_status_string(int status);
+
+/* The hipError_t value behind the calling thread's most recent PA_ERR_HIP. */
+int pa_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int pa_version(void);
+
+typedef struct pa_geom {
+  int32_t num_pages;    /* physical pages in each pool */
+  int32_t block_size;   /* tokens per page: 16 or 32 */
+  int32_t num_q_heads;  /* query heads */
+  int32_t num_kv_heads; /* KV heads */
+  int32_t head_dim;     /* 64 */
+} pa_geom_t;
+
+/* PA_OK if `g` is supported, else PA_ERR_UNSUPPORTED (or PA_ERR_INVALID_ARG for
+ * non-positive fields). */
+int pa_geom_check(pa_geom_t g);
+
+/* Bytes of one page of one pool (K or V) of one layer:
+ * block_size * num_kv_heads * head_dim * 2.  16384 for 16 tokens at 8 x 64 ([实战]
+ * §内存池管理).  0 if a field is non-positive. */
+size_t pa_page_bytes(pa_geom_t g);
+
+/* ---------------------------------------------------------------------------------
+ * Host page pool: the free-page list of [实战] §内存池管理, with a reference count per
+ * page so prefix pages can be shared (same section: different requests may share
+ * pages).  It owns host metadata only -- no device memory.  Calls on one pool are
+ * serialised internally (thread-safe).
+ * ------------------------------------------------------------------------------- */
+typedef struct pa_pool pa_pool_t;
+
+/* Create a pool of `num_pages` free pages (ids 0..num_pages-1).  *out receives the
+ * handle.  PA_ERR_INVALID_ARG if num_pages <= 0 or out is NULL. */
+int pa_pool_create(int32_t num_pages, pa_pool_t** out);
+
+/* Destroy a pool (NULL is ignored). */
+void pa_pool_destroy(pa_pool_t* p);
+
+/* Take `n` pages off the free list into ids_out[0..n-1], each with reference count 1.
+ * All or nothing: PA_ERR_OUT_OF_PAGES leaves the pool unchanged. */
+int pa_pool_alloc(pa_pool_t* p, int32_t n, int32_t* ids_out);
+
+/* Add one reference to each of the `n` allocated pages in `ids` (a prefix shared by
+ * one more sequence).  PA_ERR_INVALID_ARG (and no change) if any id is out of range
+ * or free. */
+int pa_pool_share(pa_pool_t* p, int32_t n, const int32_t* ids);
+
+/* Drop one reference from each page in `ids`; a page whose count reaches 0 returns to
+ * the free list.  PA_ERR_INVALID_ARG (and no change) if any id is out of range or
+ * already free, counting repeats within `ids`. */
+int pa_pool_free(pa_pool_t* p, int32_t n, const int32_t* ids);
+
+/* Pages currently on the free list (-1 for a NULL pool). */
+int32_t pa_pool_num_free(const pa_pool_t* p);
+
+/* Reference count of page `id` (0 = free; -1 for a bad pool or id). */
+int32_t pa_pool_refcount(const pa_pool_t* p, int32_t id);
+
+/* ---------------------------------------------------------------------------------
+ * kv_append ([guide] §推理流程：从Prefill到Decode: a token's K/V goes into the cache
+ * before the token attends).  Copies n_new_tokens rows of k_new/v_new into the pools,
+ * bit for bit.  Rows are packed by sequence: rows cu_new_lens[s] .. cu_new_lens[s+1]-1
+ * belong to sequence s, whose length after the append is ctx_lens[s]; row j of that
+ * range lands at position ctx_lens[s] - n_s + j, i.e. in page
+ * block_tables[s][pos / block_size], slot pos % block_size.
+ *   k_new, v_new   [n_new_tokens][num_kv_heads][head_dim] bf16 (device)
+ *   k_pool, v_pool pools (device, written in place)
+ *   cu_new_lens    int32 [n_seqs+1] (device), cu_new_lens[0] = 0,
+ *                  cu_new_lens[n_seqs] = n_new_tokens
+ *   ctx_lens       int32 [n_seqs] (device), lengths after the append
+ * No two rows of one call may target the same slot.  n_new_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------------- */
+int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool,
+                 void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* cu_new_lens, const int32_t* ctx_lens, int32_t n_seqs,
+                 int32_t n_new_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Decode ([guide] §推理流程, §在线Softmax): one query row per sequence, the newest
+ * token at position ctx_lens[s]-1, attending to all ctx_lens[s] keys (so the token's
+ * own K/V must already be appended).  For each (sequence, KV head) the kernel streams
+ * the sequence's pages once for all query heads of the group, keeping a running max
+ * and running sum per head; with more than one KV partition the partial results
+ * (max, sum, unnormalised output; fp32) go to `workspace` and a second kernel merges
+ * them by log-sum-exp.
+ *   out, q          [n_seqs][num_q_heads][head_dim] bf16 (device)
+ *   ctx_lens        int32 [n_seqs] (device); 0 gives a zero row
+ *   max_ctx_len     host upper bound of ctx_lens (1 <= max_ctx_len <=
+ *                   max_blocks_per_seq * block_size); it sizes the grid
+ *   scale           multiplies q.k before the softmax (1/sqrt(head_dim) = 0.125)
+ *   partition_tokens  KV tokens per partition: 0 = choose automatically, else a
+ *                   positive multiple of 256
+ *   workspace       device scratch of at least pa_decode_workspace_bytes(...) bytes
+ *                   for the same arguments; may be NULL when that size is 0
+ * ------------------------------------------------------------------------------- */
+int32_t pa_decode_partition_tokens(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,
+                                   int32_t partition_tokens);
+size_t pa_decode_workspace_bytes(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,
+                                 int32_t partition_tokens);
+int pa_decode(pa_geom_t g, void* out, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* ctx_lens,
+              int32_t n_seqs, int32_t max_ctx_len, float scale, int32_t partition_tokens,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Prefill, whole prompts or chunks ([guide] §推理流程: prefill handles every prompt
+ * token in parallel; [实战] §算子融合: tiled attention with online softmax never
+ * materialises the seq x seq score matrix).  Query rows are packed by sequence: rows
+ * cu_q_lens[s] .. cu_q_lens[s+1]-1 belong to sequence s; row i of it sits at position
+ * ctx_lens[s] - q_len_s + i and sees keys 0..position (causal != 0) or all
+ * ctx_lens[s] keys (causal == 0).  Keys before the chunk come from earlier appends,
+ * so a chunk attends to the cached prefix.  Matrix products run on bf16 MFMA with fp32
+ * accumulation.
+ *   out, q      [n_q_tokens][num_q_heads][head_dim] bf16 (device),
+ *               n_q_tokens = cu_q_lens[n_seqs]
+ *   cu_q_lens   int32 [n_seqs+1] (device); q_len_s <= ctx_lens[s] required
+ *   max_q_len   host upper bound of q_len_s (sizes the grid)
+ *   max_ctx_len host upper bound of ctx_lens (<= max_blocks_per_seq * block_size)
+ * ------------------------------------------------------------------------------- */
+int pa_prefill(pa_geom_t g, void* out, const void* q, const void* k_pool, const void* v_pool,
+               const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* cu_q_lens, const int32_t* ctx_lens, int32_t n_seqs,
+               int32_t max_q_len, int32_t max_ctx_len, float scale, int32_t causal,
+               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_PA_H */

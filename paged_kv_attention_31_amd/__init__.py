@@ -1,0 +1,235 @@
+"""paged_kv_attention_31_amd -- paged KV attention for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libpagedattn.so`` (``include/pa.h``).  It only
+marshals arguments: PyTorch tensors supply device memory and the current HIP stream,
+and every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library has not been built, every call raises.
+
+Layout (per layer; bf16 = torch.bfloat16):
+    k_pool  [num_pages, page_elems]  page = [Hkv][head_dim/8][block_size][8]
+    v_pool  [num_pages, page_elems]  page = [Hkv][head_dim][block_size]
+    block_tables int32 [n_seqs, max_blocks]; ctx_lens int32 [n_seqs]
+    q / out / k_new / v_new: token-major [tokens, heads, head_dim] bf16
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional, Sequence
+
+from . import _lib
+
+__all__ = [
+    "PagedAttnError", "Geometry", "PagePool", "page_bytes", "kv_append",
+    "decode_partition_tokens", "decode_workspace_bytes", "decode", "prefill", "library",
+]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _lib.load()
+        msg = lib.pa_status_string(status).decode()
+        if status == _lib.PA_ERR_HIP:
+            msg += f" (hipError {lib.pa_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{status}]")
+        self.status = status
+
+
+def library():
+    """The loaded ctypes library (raises if it was not built)."""
+    return _lib.load()
+
+
+def _check(status: int, where: str) -> None:
+    if status != _lib.PA_OK:
+        raise PagedAttnError(status, where)
+
+
+@dataclasses.dataclass(frozen=True)
+class Geometry:
+    num_pages: int
+    block_size: int
+    num_q_heads: int = 32
+    num_kv_heads: int = 8
+    head_dim: int = 64
+
+    def c(self) -> _lib.PaGeom:
+        return _lib.PaGeom(self.num_pages, self.block_size, self.num_q_heads, self.num_kv_heads,
+                           self.head_dim)
+
+    @property
+    def page_elems(self) -> int:
+        return self.block_size * self.num_kv_heads * self.head_dim
+
+
+def page_bytes(geom: Geometry) -> int:
+    return int(_lib.load().pa_page_bytes(geom.c()))
+
+
+# ---------------------------------------------------------------------------------------
+# host page pool
+# ---------------------------------------------------------------------------------------
+class PagePool:
+    """Free-page list with reference counts (host metadata only)."""
+
+    def __init__(self, num_pages: int):
+        self._lib = _lib.load()
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_pool_create(int(num_pages), ctypes.byref(h)), "pa_pool_create")
+        self._h = h
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pa_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _ids(ids: Sequence[int]):
+        arr = (ctypes.c_int32 * len(ids))(*[int(i) for i in ids])
+        return arr
+
+    def alloc(self, n: int) -> list[int]:
+        out = (ctypes.c_int32 * max(1, n))()
+        _check(self._lib.pa_pool_alloc(self._h, int(n), out), "pa_pool_alloc")
+        return list(out[:n])
+
+    def share(self, ids: Sequence[int]) -> None:
+        _check(self._lib.pa_pool_share(self._h, len(ids), self._ids(ids)), "pa_pool_share")
+
+    def free(self, ids: Sequence[int]) -> None:
+        _check(self._lib.pa_pool_free(self._h, len(ids), self._ids(ids)), "pa_pool_free")
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_pool_num_free(self._h))
+
+    def refcount(self, page: int) -> int:
+        return int(self._lib.pa_pool_refcount(self._h, int(page)))
+
+
+# ---------------------------------------------------------------------------------------
+# device entry points
+# ---------------------------------------------------------------------------------------
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(cond: bool, what: str) -> None:
+    if not cond:
+        raise ValueError(what)
+
+
+def _dev(t, name, dtype, numel=None, dims=None):
+    import torch
+
+    _need(t is not None and isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.is_cuda, f"{name} must be a device tensor")
+    _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if numel is not None:
+        _need(t.numel() == numel, f"{name} has {t.numel()} elements, expected {numel}")
+    if dims is not None:
+        _need(t.dim() == dims, f"{name} must have {dims} dims")
+
+
+def kv_append(geom: Geometry, k_new, v_new, k_pool, v_pool, block_tables, cu_new_lens,
+              ctx_lens, stream=None) -> None:
+    """Write rows ``k_new``/``v_new`` [T, Hkv, d] into the pools (see pa_kv_append)."""
+    import torch
+
+    n_seqs = int(ctx_lens.numel())
+    t = int(k_new.shape[0]) if k_new.dim() > 0 else 0
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        _dev(x, name, torch.bfloat16, t * geom.num_kv_heads * geom.head_dim)
+    for name, x in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(x, name, torch.bfloat16, geom.num_pages * geom.page_elems)
+    _dev(block_tables, "block_tables", torch.int32, dims=2)
+    _dev(cu_new_lens, "cu_new_lens", torch.int32, n_seqs + 1)
+    _dev(ctx_lens, "ctx_lens", torch.int32, n_seqs)
+    _need(block_tables.shape[0] == n_seqs, "block_tables rows != n_seqs")
+    st = _lib.load().pa_kv_append(geom.c(), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                  _ptr(block_tables), int(block_tables.shape[1]),
+                                  _ptr(cu_new_lens), _ptr(ctx_lens), n_seqs, t, _stream(stream))
+    _check(st, "pa_kv_append")
+
+
+def decode_partition_tokens(geom: Geometry, n_seqs: int, max_ctx_len: int,
+                            partition_tokens: int = 0) -> int:
+    r = int(_lib.load().pa_decode_partition_tokens(geom.c(), n_seqs, max_ctx_len,
+                                                    partition_tokens))
+    _check(min(r, 0), "pa_decode_partition_tokens")
+    return r
+
+
+def decode_workspace_bytes(geom: Geometry, n_seqs: int, max_ctx_len: int,
+                           partition_tokens: int = 0) -> int:
+    return int(_lib.load().pa_decode_workspace_bytes(geom.c(), n_seqs, max_ctx_len,
+                                                     partition_tokens))
+
+
+def decode(geom: Geometry, out, q, k_pool, v_pool, block_tables, ctx_lens, max_ctx_len: int,
+           scale: float, partition_tokens: int = 0, workspace=None, stream=None) -> None:
+    """One query row per sequence over its paged context (see pa_decode).  ``workspace``
+    is a uint8 device tensor of at least ``decode_workspace_bytes`` bytes (allocated here
+    when omitted)."""
+    import torch
+
+    n = int(ctx_lens.numel())
+    rows = n * geom.num_q_heads * geom.head_dim
+    _dev(out, "out", torch.bfloat16, rows)
+    _dev(q, "q", torch.bfloat16, rows)
+    for name, x in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(x, name, torch.bfloat16, geom.num_pages * geom.page_elems)
+    _dev(block_tables, "block_tables", torch.int32, dims=2)
+    _dev(ctx_lens, "ctx_lens", torch.int32, n)
+    _need(block_tables.shape[0] == n, "block_tables rows != n_seqs")
+    need = decode_workspace_bytes(geom, n, int(max_ctx_len), int(partition_tokens))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    st = _lib.load().pa_decode(geom.c(), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                               _ptr(block_tables), int(block_tables.shape[1]), _ptr(ctx_lens), n,
+                               int(max_ctx_len), float(scale), int(partition_tokens),
+                               _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "pa_decode")
+
+
+def prefill(geom: Geometry, out, q, k_pool, v_pool, block_tables, cu_q_lens, ctx_lens,
+            max_q_len: int, max_ctx_len: int, scale: float, causal: bool = True,
+            stream=None) -> None:
+    """Packed query rows over their sequences' paged contexts (see pa_prefill)."""
+    import torch
+
+    n = int(ctx_lens.numel())
+    tq = int(q.shape[0]) if q.dim() > 0 else 0
+    rows = tq * geom.num_q_heads * geom.head_dim
+    _dev(out, "out", torch.bfloat16, rows)
+    _dev(q, "q", torch.bfloat16, rows)
+    for name, x in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(x, name, torch.bfloat16, geom.num_pages * geom.page_elems)
+    _dev(block_tables, "block_tables", torch.int32, dims=2)
+    _dev(cu_q_lens, "cu_q_lens", torch.int32, n + 1)
+    _dev(ctx_lens, "ctx_lens", torch.int32, n)
+    _need(block_tables.shape[0] == n, "block_tables rows != n_seqs")
+    st = _lib.load().pa_prefill(geom.c(), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                _ptr(block_tables), int(block_tables.shape[1]), _ptr(cu_q_lens),
+                                _ptr(ctx_lens), n, int(max_q_len), int(max_ctx_len), float(scale),
+                                1 if causal else 0, _stream(stream))
+    _check(st, "pa_prefill")

@@ -1,0 +1,75 @@
+"""ctypes view of libpagedattn.so (the C ABI in include/pa.h)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = -1
+PA_ERR_OUT_OF_PAGES = -2
+PA_ERR_UNSUPPORTED = -3
+PA_ERR_WORKSPACE = -4
+PA_ERR_HIP = -5
+
+
+class PaGeom(ctypes.Structure):
+    _fields_ = [
+        ("num_pages", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
+_c_i32 = ctypes.c_int32
+_c_p = ctypes.c_void_p
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_hip_error": (ctypes.c_int, []),
+    "pa_version": (ctypes.c_int, []),
+    "pa_geom_check": (ctypes.c_int, [PaGeom]),
+    "pa_page_bytes": (ctypes.c_size_t, [PaGeom]),
+    "pa_pool_create": (ctypes.c_int, [_c_i32, ctypes.POINTER(_c_p)]),
+    "pa_pool_destroy": (None, [_c_p]),
+    "pa_pool_alloc": (ctypes.c_int, [_c_p, _c_i32, _c_i32p]),
+    "pa_pool_share": (ctypes.c_int, [_c_p, _c_i32, _c_i32p]),
+    "pa_pool_free": (ctypes.c_int, [_c_p, _c_i32, _c_i32p]),
+    "pa_pool_num_free": (_c_i32, [_c_p]),
+    "pa_pool_refcount": (_c_i32, [_c_p, _c_i32]),
+    "pa_kv_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p,
+                                    _c_i32, _c_i32, _c_p]),
+    "pa_decode_partition_tokens": (_c_i32, [PaGeom, _c_i32, _c_i32, _c_i32]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [PaGeom, _c_i32, _c_i32, _c_i32]),
+    "pa_decode": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32,
+                                 _c_i32, ctypes.c_float, _c_i32, _c_p, ctypes.c_size_t, _c_p]),
+    "pa_prefill": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p,
+                                  _c_i32, _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_p]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_kv_attention_31_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

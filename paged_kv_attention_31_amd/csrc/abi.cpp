@@ -1,0 +1,248 @@
+// C ABI of libpagedattn (declared in include/pa.h): argument validation, the host page
+// pool, split-K sizing, and dispatch to the HIP launchers.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return PA_ERR_HIP;
+}
+
+pa::LaunchGeom to_launch(const pa_geom_t& g) {
+  return pa::LaunchGeom{g.num_pages, g.block_size, g.num_q_heads, g.num_kv_heads};
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tokens per decode partition.  Explicit values are kept (validated by the caller);
+// otherwise split so that (sequences x KV heads x partitions) gives the chip enough
+// workgroups (256 CUs, several resident workgroups each) without making partitions so
+// short that the merge traffic matters.
+int32_t choose_partition(const pa_geom_t& g, int32_t n_seqs, int32_t max_ctx_len,
+                         int32_t requested) {
+  const int32_t q = pa::kDecodePartQuantum;
+  const int64_t quanta = std::max<int64_t>(1, ceil_div(std::max(max_ctx_len, 1), q));
+  if (requested > 0) return requested;
+  const int64_t units = std::max<int64_t>(1, (int64_t)n_seqs * g.num_kv_heads);
+  constexpr int64_t kTargetBlocks = 4096;
+  int64_t f = std::max<int64_t>(1, (units * quanta) / kTargetBlocks);
+  f = std::min(f, quanta);
+  return (int32_t)(f * q);
+}
+
+int32_t num_parts(int32_t max_ctx_len, int32_t part) {
+  return (int32_t)std::max<int64_t>(1, ceil_div(std::max(max_ctx_len, 0), part));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// pool
+// ---------------------------------------------------------------------------------------
+struct pa_pool {
+  std::mutex mu;
+  std::vector<int32_t> free_list;  // LIFO stack of free page ids
+  std::vector<int32_t> refs;       // reference count per page (0 = free)
+};
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_OUT_OF_PAGES: return "out of pages";
+    case PA_ERR_UNSUPPORTED: return "unsupported geometry";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int pa_last_hip_error(void) { return g_last_hip_error; }
+
+int pa_version(void) { return 10000; }
+
+int pa_geom_check(pa_geom_t g) {
+  if (g.num_pages <= 0 || g.block_size <= 0 || g.num_q_heads <= 0 || g.num_kv_heads <= 0 ||
+      g.head_dim <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (g.head_dim != pa::kHeadDim) return PA_ERR_UNSUPPORTED;
+  if (g.block_size != 16 && g.block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (g.num_q_heads != pa::kGroup * g.num_kv_heads) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+size_t pa_page_bytes(pa_geom_t g) {
+  if (g.block_size <= 0 || g.num_kv_heads <= 0 || g.head_dim <= 0) return 0;
+  return (size_t)g.block_size * g.num_kv_heads * g.head_dim * 2;
+}
+
+int pa_pool_create(int32_t num_pages, pa_pool_t** out) {
+  if (!out || num_pages <= 0) return PA_ERR_INVALID_ARG;
+  pa_pool* p = new (std::nothrow) pa_pool();
+  if (!p) return PA_ERR_INVALID_ARG;
+  p->refs.assign(num_pages, 0);
+  p->free_list.resize(num_pages);
+  // pop order: 0, 1, 2, ... (the stack top is the back)
+  for (int32_t i = 0; i < num_pages; ++i) p->free_list[i] = num_pages - 1 - i;
+  *out = p;
+  return PA_OK;
+}
+
+void pa_pool_destroy(pa_pool_t* p) { delete p; }
+
+int pa_pool_alloc(pa_pool_t* p, int32_t n, int32_t* ids_out) {
+  if (!p || n < 0 || (n > 0 && !ids_out)) return PA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(p->mu);
+  if ((size_t)n > p->free_list.size()) return PA_ERR_OUT_OF_PAGES;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t id = p->free_list.back();
+    p->free_list.pop_back();
+    p->refs[id] = 1;
+    ids_out[i] = id;
+  }
+  return PA_OK;
+}
+
+int pa_pool_share(pa_pool_t* p, int32_t n, const int32_t* ids) {
+  if (!p || n < 0 || (n > 0 && !ids)) return PA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(p->mu);
+  const int32_t np = (int32_t)p->refs.size();
+  for (int32_t i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= np || p->refs[ids[i]] <= 0) return PA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) ++p->refs[ids[i]];
+  return PA_OK;
+}
+
+int pa_pool_free(pa_pool_t* p, int32_t n, const int32_t* ids) {
+  if (!p || n < 0 || (n > 0 && !ids)) return PA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(p->mu);
+  const int32_t np = (int32_t)p->refs.size();
+  // validate first (counting repeats) so a bad call changes nothing
+  std::vector<int32_t> drop;
+  drop.reserve(n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= np) return PA_ERR_INVALID_ARG;
+    drop.push_back(ids[i]);
+  }
+  std::sort(drop.begin(), drop.end());
+  for (size_t i = 0; i < drop.size();) {
+    size_t k = i;
+    while (k < drop.size() && drop[k] == drop[i]) ++k;
+    if ((int64_t)(k - i) > p->refs[drop[i]]) return PA_ERR_INVALID_ARG;
+    i = k;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    if (--p->refs[ids[i]] == 0) p->free_list.push_back(ids[i]);
+  }
+  return PA_OK;
+}
+
+int32_t pa_pool_num_free(const pa_pool_t* p) {
+  if (!p) return -1;
+  std::lock_guard<std::mutex> lock(const_cast<pa_pool*>(p)->mu);
+  return (int32_t)p->free_list.size();
+}
+
+int32_t pa_pool_refcount(const pa_pool_t* p, int32_t id) {
+  if (!p) return -1;
+  std::lock_guard<std::mutex> lock(const_cast<pa_pool*>(p)->mu);
+  if (id < 0 || id >= (int32_t)p->refs.size()) return -1;
+  return p->refs[id];
+}
+
+// ---------------------------------------------------------------------------------------
+// device entry points
+// ---------------------------------------------------------------------------------------
+int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* cu_new_lens, const int32_t* ctx_lens, int32_t n_seqs,
+                 int32_t n_new_tokens, void* stream) {
+  int st = pa_geom_check(g);
+  if (st != PA_OK) return st;
+  if (n_new_tokens < 0 || n_seqs < 0 || max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if (n_new_tokens == 0) return PA_OK;
+  if (n_seqs == 0) return PA_ERR_INVALID_ARG;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !cu_new_lens || !ctx_lens)
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)n_new_tokens * g.num_kv_heads > (int64_t)INT32_MAX - 4) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_kv_append(to_launch(g), k_new, v_new, k_pool, v_pool, block_tables,
+                                         max_blocks_per_seq, cu_new_lens, ctx_lens, n_seqs,
+                                         n_new_tokens, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_partition_tokens(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,
+                                   int32_t partition_tokens) {
+  if (pa_geom_check(g) != PA_OK || n_seqs < 0 || max_ctx_len < 0) return PA_ERR_INVALID_ARG;
+  if (partition_tokens < 0 || partition_tokens % pa::kDecodePartQuantum != 0)
+    return PA_ERR_INVALID_ARG;
+  return choose_partition(g, n_seqs, max_ctx_len, partition_tokens);
+}
+
+size_t pa_decode_workspace_bytes(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,
+                                 int32_t partition_tokens) {
+  const int32_t part = pa_decode_partition_tokens(g, n_seqs, max_ctx_len, partition_tokens);
+  if (part <= 0) return 0;
+  return pa::decode_workspace_bytes(n_seqs, num_parts(max_ctx_len, part), g.num_q_heads);
+}
+
+int pa_decode(pa_geom_t g, void* out, const void* q, const void* k_pool, const void* v_pool,
+              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* ctx_lens,
+              int32_t n_seqs, int32_t max_ctx_len, float scale, int32_t partition_tokens,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = pa_geom_check(g);
+  if (st != PA_OK) return st;
+  if (n_seqs < 0 || max_blocks_per_seq <= 0 || max_ctx_len < 0) return PA_ERR_INVALID_ARG;
+  if ((int64_t)max_ctx_len > (int64_t)max_blocks_per_seq * g.block_size) return PA_ERR_INVALID_ARG;
+  if (partition_tokens < 0 || partition_tokens % pa::kDecodePartQuantum != 0)
+    return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (n_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !ctx_lens) return PA_ERR_INVALID_ARG;
+  const int32_t part = choose_partition(g, n_seqs, max_ctx_len, partition_tokens);
+  const int32_t np = num_parts(max_ctx_len, part);
+  if ((int64_t)n_seqs * g.num_kv_heads * np > (int64_t)INT32_MAX) return PA_ERR_INVALID_ARG;
+  const size_t need = pa::decode_workspace_bytes(n_seqs, np, g.num_q_heads);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  return hip_status(pa::launch_decode(to_launch(g), out, q, k_pool, v_pool, block_tables,
+                                      max_blocks_per_seq, ctx_lens, n_seqs, np, part, scale,
+                                      workspace, static_cast<hipStream_t>(stream)));
+}
+
+int pa_prefill(pa_geom_t g, void* out, const void* q, const void* k_pool, const void* v_pool,
+               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+               const int32_t* ctx_lens, int32_t n_seqs, int32_t max_q_len, int32_t max_ctx_len,
+               float scale, int32_t causal, void* stream) {
+  int st = pa_geom_check(g);
+  if (st != PA_OK) return st;
+  if (n_seqs < 0 || max_blocks_per_seq <= 0 || max_q_len < 0 || max_ctx_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)max_ctx_len > (int64_t)max_blocks_per_seq * g.block_size) return PA_ERR_INVALID_ARG;
+  if (max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (n_seqs == 0 || max_q_len == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !ctx_lens)
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)ceil_div(max_q_len, 32) * n_seqs * g.num_kv_heads > (int64_t)INT32_MAX)
+    return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_prefill(to_launch(g), out, q, k_pool, v_pool, block_tables,
+                                       max_blocks_per_seq, cu_q_lens, ctx_lens, n_seqs, max_q_len,
+                                       scale, causal, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

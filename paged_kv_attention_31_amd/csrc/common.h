@@ -1,0 +1,87 @@
+// Device helpers shared by the HIP kernels of libpagedattn (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace pa {
+
+constexpr int kWave = 64;      // CDNA wavefront width
+constexpr int kChunk = 8;      // bf16 values in one 16-byte piece of a K row
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ---- bf16 bit patterns -----------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (lowers to v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t p;
+  p[0] = (__bf16)lo;
+  p[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c on bf16 pairs, fp32 result (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---- cross-lane -----------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                            0xF, 0xF, false));
+}
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i inside each 16 lanes
+
+// All 64 lanes receive the maximum / sum over the wave.  Inside each row of 16 lanes a
+// DPP butterfly; across the four rows the row results are read back per row.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<kDppQuadSwap1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadSwap2>(x));
+  x = fmaxf(x, dpp_f<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppRowMirror>(x));
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f<kDppQuadSwap1>(x);
+  x += dpp_f<kDppQuadSwap2>(x);
+  x += dpp_f<kDppRowHalfMirror>(x);
+  x += dpp_f<kDppRowMirror>(x);
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) {
+  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, x), m, kWave));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace pa

@@ -1,0 +1,137 @@
+"""GPU-side plumbing for the parity tests: upload a generated batch, run the library
+over it, and compare with the oracle.  Test infrastructure only."""
+
+from __future__ import annotations
+
+import numpy as np
+
+import workloads as W
+
+MAX_ABS = 1e-2   # tolerance on |gpu - oracle| over all elements (fp32 compare)
+MEAN_ABS = 1e-3  # tolerance on mean |gpu - oracle|
+
+
+def torch_mod():
+    import torch
+
+    return torch
+
+
+def dev():
+    return torch_mod().device("cuda:0")
+
+
+def bf16_dev(bits: np.ndarray):
+    t = torch_mod()
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return t.from_numpy(a).to(dev()).view(t.bfloat16)
+
+
+def i32_dev(a: np.ndarray):
+    t = torch_mod()
+    return t.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev())
+
+
+def bits_host(x) -> np.ndarray:
+    """bf16 device tensor -> uint16 numpy bits."""
+    t = torch_mod()
+    return x.contiguous().view(t.int16).cpu().numpy().view(np.uint16)
+
+
+def f32_host(x) -> np.ndarray:
+    return x.float().cpu().numpy()
+
+
+def geometry(case: W.Case):
+    import paged_kv_attention_31_amd as pa
+
+    return pa.Geometry(case.num_pages, case.block_size, case.num_q_heads, case.num_kv_heads,
+                       case.head_dim)
+
+
+def sentinel_pools(case: W.Case):
+    t = torch_mod()
+    e = W.page_elems(case)
+    k = t.full((case.num_pages, e), W.SENTINEL_BITS, dtype=t.int16, device=dev()).view(t.bfloat16)
+    v = t.full((case.num_pages, e), W.SENTINEL_BITS, dtype=t.int16, device=dev()).view(t.bfloat16)
+    return k, v
+
+
+class GpuCase:
+    """A generated batch on the device, with the library's pools after setup + step
+    appends."""
+
+    def __init__(self, case: W.Case, pools=None):
+        import paged_kv_attention_31_amd as pa
+
+        self.case = case
+        self.geom = geometry(case)
+        self.bt = i32_dev(case.block_tables)
+        self.ctx = i32_dev(case.ctx_lens)
+        self.kp, self.vp = pools if pools is not None else sentinel_pools(case)
+        hkv, d = case.num_kv_heads, case.head_dim
+        if case.k_setup.shape[0]:
+            pa.kv_append(self.geom, bf16_dev(case.k_setup), bf16_dev(case.v_setup), self.kp,
+                         self.vp, self.bt, i32_dev(case.cu_setup_lens),
+                         i32_dev(case.setup_ctx_lens))
+        self.k_new = bf16_dev(case.k_new.reshape(-1, hkv, d))
+        self.v_new = bf16_dev(case.v_new.reshape(-1, hkv, d))
+        self.cu_new = i32_dev(case.cu_new_lens)
+        self.append_step()
+        r = case.decode_seqs
+        self.dec_bt = self.bt[r.start:r.stop]
+        self.dec_ctx = self.ctx[r.start:r.stop]
+        r = case.prefill_seqs
+        self.pre_bt = self.bt[r.start:r.stop]
+        self.pre_ctx = self.ctx[r.start:r.stop]
+        self.q_dec = bf16_dev(case.q_decode) if len(case.decode_seqs) else None
+        self.q_pre = bf16_dev(case.q_prefill) if len(case.prefill_seqs) else None
+        self.cu_q = i32_dev(case.cu_q_lens_prefill)
+
+    def append_step(self):
+        import paged_kv_attention_31_amd as pa
+
+        if self.case.k_new.shape[0]:
+            pa.kv_append(self.geom, self.k_new, self.v_new, self.kp, self.vp, self.bt,
+                         self.cu_new, self.ctx)
+
+    def decode(self, partition_tokens: int = 0, max_ctx=None):
+        import paged_kv_attention_31_amd as pa
+
+        t = torch_mod()
+        c = self.case
+        r = c.decode_seqs
+        out = t.empty((len(r), c.num_q_heads, c.head_dim), dtype=t.bfloat16, device=dev())
+        mc = int(c.ctx_lens[r.start:r.stop].max()) if max_ctx is None else max_ctx
+        pa.decode(self.geom, out, self.q_dec, self.kp, self.vp, self.dec_bt, self.dec_ctx, mc,
+                  c.scale, partition_tokens=partition_tokens)
+        return out
+
+    def prefill(self, causal: bool = True):
+        import paged_kv_attention_31_amd as pa
+
+        t = torch_mod()
+        c = self.case
+        ql = c.q_lens_prefill
+        out = t.empty((int(ql.sum()), c.num_q_heads, c.head_dim), dtype=t.bfloat16, device=dev())
+        r = c.prefill_seqs
+        pa.prefill(self.geom, out, self.q_pre, self.kp, self.vp, self.pre_bt, self.cu_q,
+                   self.pre_ctx, int(ql.max()), int(c.ctx_lens[r.start:r.stop].max()), c.scale,
+                   causal=causal)
+        return out
+
+
+def errors(gpu_out, ref_f64: np.ndarray):
+    """(max-abs, mean-abs) of the bf16 GPU output (widened to fp32) against the oracle's
+    fp64 result rounded to fp32."""
+    g = f32_host(gpu_out).astype(np.float32)
+    r = ref_f64.astype(np.float32)
+    diff = np.abs(g - r).astype(np.float64)
+    return float(np.max(diff)) if diff.size else 0.0, float(np.mean(diff)) if diff.size else 0.0
+
+
+def assert_close(gpu_out, ref_f64: np.ndarray, what: str = ""):
+    mx, mean = errors(gpu_out, ref_f64)
+    assert np.isfinite(mx), f"{what}: non-finite output"
+    assert mx <= MAX_ABS and mean <= MEAN_ABS, f"{what}: max-abs {mx:.3e} mean-abs {mean:.3e}"
+    return mx, mean

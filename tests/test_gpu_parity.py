@@ -1,0 +1,250 @@
+"""Parity of the HIP library against the CPU oracle on the GPU (marked ``gpu``).
+
+Every output is compared element by element with the oracle on the same seeded inputs:
+bf16 outputs widened to fp32 against the fp64 oracle rounded to fp32, max-abs <= 1e-2
+and mean-abs <= 1e-3; kv_append must reproduce the oracle's pools bit for bit (sentinel
+bytes included).  The two full-size workloads (16 x 32768 decode; one layer of the
+mixed step) are checked on sampled sequences, in the launch configuration the bench
+uses."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.gpu_helpers import GpuCase, assert_close, bits_host
+from tests.helpers import oracle_decode, oracle_pools, oracle_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------------------------------
+# kv_append: bit exact
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_kv_append_bit_exact_workloads(cfg):
+    case = W.make_case(cfg)
+    _announce(f"kv_append workload {cfg}")
+    g = GpuCase(case)
+    kp, vp = oracle_pools(case)
+    assert np.array_equal(bits_host(g.kp), kp)
+    assert np.array_equal(bits_host(g.vp), vp)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_kv_append_bit_exact_ragged(bs):
+    case = W.custom_case([1, 31, 32, 33, 100, 7], [1, 31, 5, 33, 64, 2], kind="prefill",
+                         block_size=bs, seed=40 + bs)
+    _announce(f"kv_append ragged bs={bs}")
+    g = GpuCase(case)
+    kp, vp = oracle_pools(case)
+    assert np.array_equal(bits_host(g.kp), kp)
+    assert np.array_equal(bits_host(g.vp), vp)
+
+
+# ---------------------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_decode_workload_parity(cfg):
+    case = W.make_case(cfg)
+    _announce(f"decode workload {cfg}")
+    g = GpuCase(case)
+    out = g.decode()
+    kp, vp = oracle_pools(case)
+    ref = oracle_decode(case, kp, vp)
+    mx, mean = assert_close(out, ref, f"decode cfg{cfg}")
+    _announce(f"decode workload {cfg}: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+SWEEP_CTX = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 255, 256, 257, 300, 511, 512, 513,
+             1000, 1025]
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("part", [0, 256, 512])
+def test_decode_length_sweep(bs, part):
+    case = W.custom_case(SWEEP_CTX, [1] * len(SWEEP_CTX), block_size=bs, seed=50 + bs)
+    _announce(f"decode sweep bs={bs} part={part}")
+    g = GpuCase(case)
+    out = g.decode(partition_tokens=part)
+    kp, vp = oracle_pools(case)
+    ref = oracle_decode(case, kp, vp)
+    assert_close(out, ref, f"sweep bs={bs} part={part}")
+
+
+def test_decode_empty_context_and_loose_max_ctx():
+    case = W.custom_case([0, 5, 0, 40], [0, 1, 0, 1], block_size=16, seed=60)
+    _announce("decode empty contexts")
+    g = GpuCase(case)
+    kp, vp = oracle_pools(case)
+    ref = oracle_decode(case, kp, vp)
+    for part in (0, 256):
+        out = g.decode(partition_tokens=part, max_ctx=case.max_blocks * 16)
+        assert_close(out, ref, "empty contexts")
+        assert np.all(bits_host(out[0]) == 0) and np.all(bits_host(out[2]) == 0)
+
+
+def test_decode_context_one_returns_v_exactly():
+    case = W.custom_case([1, 1, 1], [1, 1, 1], block_size=32, seed=61, sigma_q=4.0)
+    _announce("decode ctx=1")
+    g = GpuCase(case)
+    out = bits_host(g.decode())
+    for s in range(3):
+        v0 = case.v_new[case.cu_new_lens[s]]  # [Hkv, d] bits
+        for h in range(32):
+            assert np.array_equal(out[s, h], v0[h // 4])
+
+
+def test_decode_page_permutation_shared_prefix_and_determinism():
+    case = W.custom_case([300, 97, 33, 800], [1, 1, 1, 1], block_size=16, seed=62,
+                         shared_seqs=[0, 3], shared_prefix_tokens=32, slack=1.0)
+    _announce("decode invariants")
+    g = GpuCase(case)
+    ref = bits_host(g.decode(partition_tokens=256))
+    assert np.array_equal(ref, bits_host(g.decode(partition_tokens=256)))  # run to run
+    # physical page permutation with the block table rewritten: bit-identical
+    perm = np.random.default_rng(5).permutation(case.num_pages)
+    kp_h, vp_h = bits_host(g.kp), bits_host(g.vp)
+    kp2, vp2 = np.empty_like(kp_h), np.empty_like(vp_h)
+    kp2[perm] = kp_h
+    vp2[perm] = vp_h
+    import torch
+
+    from tests.gpu_helpers import bf16_dev, i32_dev
+    g.kp.copy_(bf16_dev(kp2))
+    g.vp.copy_(bf16_dev(vp2))
+    g.dec_bt = i32_dev(perm[case.block_tables])
+    assert np.array_equal(ref, bits_host(g.decode(partition_tokens=256)))
+    # shared prefix pages vs private copies of the same bytes: bit-identical
+    bt = perm[case.block_tables].copy()
+    used = set(bt.ravel().tolist())
+    free = [p for p in range(case.num_pages) if p not in used]
+    for b in range(2):
+        src = bt[3, b]
+        g.kp[free[b]].copy_(g.kp[src])
+        g.vp[free[b]].copy_(g.vp[src])
+        bt[3, b] = free[b]
+    g.dec_bt = i32_dev(bt)
+    torch.cuda.synchronize()
+    assert np.array_equal(ref, bits_host(g.decode(partition_tokens=256)))
+
+
+def test_decode_zero_query_is_mean_of_v():
+    case = W.custom_case([200, 5], [1, 1], block_size=32, seed=63)
+    case.q_decode[:] = 0
+    g = GpuCase(case)
+    out = g.decode()
+    for s in range(2):
+        _, vl = case.logical_kv(s)
+        mean = O.bf16_to_f64(vl).mean(axis=0)
+        ref = np.repeat(mean, 4, axis=0)[None]
+        assert_close(out[s:s + 1], ref, "q=0")
+
+
+def test_decode_long_context_workload_sampled():
+    """16 x 32768 tokens, block size 32, split-K with the automatic partition."""
+    case = W.make_case(4)
+    _announce("decode workload 4 (16 x 32768), sampled")
+    g = GpuCase(case)
+    out = g.decode()
+    kp_h, vp_h = bits_host(g.kp), bits_host(g.vp)
+    for s in (0, 7, 15):
+        kl, vl = case.logical_kv(s)
+        # the library's pool holds exactly the logical rows (layout read by the oracle)
+        kb, vb = O.gather(kp_h, vp_h, case.block_tables[s], 32768, 32, 8, 64)
+        assert np.array_equal(kb, kl) and np.array_equal(vb, vl)
+        ref = O.attention(O.bf16_to_f64(case.q_decode[s:s + 1]), O.bf16_to_f64(kl),
+                          O.bf16_to_f64(vl), [32768], case.scale)
+        mx, mean = assert_close(out[s:s + 1], ref, f"cfg4 seq {s}")
+        _announce(f"cfg4 seq {s}: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+# ---------------------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------------------
+def test_prefill_workload_parity():
+    case = W.make_case(3)
+    _announce("prefill workload 3")
+    g = GpuCase(case)
+    out = g.prefill()
+    kp, vp = oracle_pools(case)
+    ref = oracle_prefill(case, kp, vp)
+    mx, mean = assert_close(out, ref, "prefill cfg3")
+    _announce(f"prefill workload 3: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_chunked_ragged(bs, causal):
+    # chunks after a cached prefix, lengths that are not multiples of the 32-row tile,
+    # a one-token chunk and a chunk that is a whole prompt
+    case = W.custom_case([70, 33, 129, 1, 200, 64], [7, 33, 100, 1, 1, 40], kind="prefill",
+                         block_size=bs, seed=70 + bs)
+    _announce(f"prefill chunked bs={bs} causal={causal}")
+    g = GpuCase(case)
+    out = g.prefill(causal=causal)
+    kp, vp = oracle_pools(case)
+    ref = oracle_prefill(case, kp, vp, causal=causal)
+    assert_close(out, ref, f"prefill bs={bs} causal={causal}")
+
+
+def test_prefill_last_row_matches_decode_and_permutation():
+    case = W.custom_case([150, 47], [150, 47], kind="prefill", block_size=16, seed=80)
+    g = GpuCase(case)
+    out = g.prefill()
+    ref_bits = bits_host(out)
+    assert np.array_equal(ref_bits, bits_host(g.prefill()))  # run to run
+    kp, vp = oracle_pools(case)
+    cu = case.cu_q_lens_prefill
+    for s in range(2):
+        dec = O.decode(case.q_prefill[cu[s + 1] - 1:cu[s + 1]], kp, vp, case.block_tables[s:s + 1],
+                       [int(case.ctx_lens[s])], 16, 8, 64, case.scale)
+        assert_close(out[cu[s + 1] - 1:cu[s + 1]], dec, "last prefill row vs decode")
+    perm = np.random.default_rng(9).permutation(case.num_pages)
+    kp_h, vp_h = bits_host(g.kp), bits_host(g.vp)
+    kp2, vp2 = np.empty_like(kp_h), np.empty_like(vp_h)
+    kp2[perm] = kp_h
+    vp2[perm] = vp_h
+    from tests.gpu_helpers import bf16_dev, i32_dev
+    g.kp.copy_(bf16_dev(kp2))
+    g.vp.copy_(bf16_dev(vp2))
+    g.pre_bt = i32_dev(perm[case.block_tables])
+    assert np.array_equal(ref_bits, bits_host(g.prefill()))
+
+
+# ---------------------------------------------------------------------------------------
+# the mixed step, one layer at full size
+# ---------------------------------------------------------------------------------------
+def test_mixed_step_layer_sampled():
+    case = W.make_case(5, layer=0)
+    _announce("mixed step layer 0 (chunk 512 + 128 decode), sampled")
+    g = GpuCase(case)
+    dec = g.decode()
+    pre = g.prefill()
+    # chunk rows: every row, against the oracle over the chunk sequence's logical K/V
+    s = case.prefill_seqs.start
+    kl, vl = case.logical_kv(s)
+    ctx = int(case.ctx_lens[s])
+    ql = int(case.new_lens[s])
+    vis = [ctx - ql + i + 1 for i in range(ql)]
+    ref = O.attention(O.bf16_to_f64(case.q_prefill), O.bf16_to_f64(kl), O.bf16_to_f64(vl), vis,
+                      case.scale)
+    mx, mean = assert_close(pre, ref, "mixed chunk")
+    _announce(f"mixed chunk: max-abs {mx:.2e} mean-abs {mean:.2e}")
+    # decode rows: shared-prefix sequences and others, through the library's pool
+    kp_h, vp_h = bits_host(g.kp), bits_host(g.vp)
+    picks = sorted(set([int(x) for x in case.shared_seqs[:3]] + [0, 1, 64, 127]))
+    for d in picks:
+        kb, vb = O.gather(kp_h, vp_h, case.block_tables[d], int(case.ctx_lens[d]), 32, 8, 64)
+        kl, vl = case.logical_kv(d)
+        assert np.array_equal(kb, kl) and np.array_equal(vb, vl)
+        ref = O.attention(O.bf16_to_f64(case.q_decode[d:d + 1]), O.bf16_to_f64(kl),
+                          O.bf16_to_f64(vl), [int(case.ctx_lens[d])], case.scale)
+        assert_close(dec[d:d + 1], ref, f"mixed decode seq {d}")
