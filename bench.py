@@ -1,0 +1,300 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Default workload: the mixed continuous-batch step over 16 layers (per layer: kv_append
+of 640 new tokens, a 512-token causal prefill chunk over 512 cached tokens, and decode
+of 128 sequences with contexts uniform in [16, 8192], the first 256 tokens of 32 of
+them on shared pages; block size 32; 32 query / 8 KV heads, head_dim 64, bf16).  It is
+the one workload that runs every step of the path (append, decode partitions, split-K
+merge, chunked prefill), so one step = one pass of the whole path.
+
+    python bench.py [--steps K] [--warmup W] [--workload mixed|decode-long|decode-batched|prefill]
+
+Prints one JSON line.  ``value`` = decode KV bytes read per step / wall time per step
+(whole step, all kernels).  ``roofline`` reports the dominant kernel (pa_decode, timed
+with HIP events on its stream) against HBM peak; ``roofline_prefill`` reports pa_prefill
+against dense bf16 MFMA peak.  ``cpu_baseline`` times the CPU oracle on a bounded sample
+of the same workload (layer 0) before the GPU is touched.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "decode KV-read GB/s (%HBM peak); prefill TFLOP/s (%MFMA peak), 1B shape"
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KV_BYTES_PER_TOKEN = 2 * 8 * 64 * 2  # K and V, 8 KV heads x 64 dims x bf16, per layer
+FLOP_PER_PAIR = 4 * 64 * 32  # QK^T and PV over 32 query heads, per visible (query, key)
+
+WORKLOADS = {
+    "mixed": 5,
+    "decode-long": 4,
+    "decode-batched": 2,
+    "prefill": 3,
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, single thread, bounded sample
+# ---------------------------------------------------------------------------------------
+def cpu_baseline(cfg: int, budget_s: float = 20.0) -> dict:
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    case = W.make_case(cfg, layer=0)
+    kp = W.sentinel_pool(case)
+    vp = W.sentinel_pool(case)
+    O.kv_append(kp, vp, case.k_setup, case.v_setup, case.block_tables, case.cu_setup_lens,
+                case.setup_ctx_lens, case.block_size)
+    O.kv_append(kp, vp, case.k_new, case.v_new, case.block_tables, case.cu_new_lens,
+                case.ctx_lens, case.block_size)
+    r = case.decode_seqs
+    with threadpool_limits(limits=1):
+        if len(r):
+            bt = case.block_tables[r.start:r.stop]
+            ctx = case.ctx_lens[r.start:r.stop]
+            done, nbytes = 0, 0
+            t0 = time.perf_counter()
+            for s in range(len(r)):
+                O.decode(case.q_decode, kp, vp, bt, ctx, case.block_size, case.num_kv_heads,
+                         case.head_dim, case.scale, seqs=[s])
+                done += 1
+                nbytes += int(ctx[s]) * KV_BYTES_PER_TOKEN
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                    "sample": f"fp64 numpy oracle decode (gather + three-pass softmax) of "
+                              f"{done} of {len(r)} decode sequences of layer 0 "
+                              f"({nbytes / 1e6:.1f} MB of KV) in {dt:.1f} s, 1 thread"}
+        p = case.prefill_seqs
+        t0 = time.perf_counter()
+        O.prefill(case.q_prefill, kp, vp, case.block_tables[p.start:p.stop],
+                  case.cu_q_lens_prefill, case.ctx_lens[p.start:p.stop], case.block_size,
+                  case.num_kv_heads, case.head_dim, case.scale)
+        dt = time.perf_counter() - t0
+        flops = case.prefill_pairs() * FLOP_PER_PAIR
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                "sample": f"fp64 numpy oracle prefill of all {len(p)} prompts in {dt:.1f} s, "
+                          f"1 thread"}
+
+
+# ---------------------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------------------
+class Layer:
+    """One layer's pools and step inputs on the device."""
+
+    def __init__(self, case: W.Case, torch, pa, bt, ctx, cu_new, cu_q):
+        dev = torch.device("cuda:0")
+
+        def up16(bits):
+            a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+            return torch.from_numpy(a).to(dev).view(torch.bfloat16)
+
+        e = W.page_elems(case)
+        self.kp = torch.zeros((case.num_pages, e), dtype=torch.bfloat16, device=dev)
+        self.vp = torch.zeros((case.num_pages, e), dtype=torch.bfloat16, device=dev)
+        self.geom = pa.Geometry(case.num_pages, case.block_size, case.num_q_heads,
+                                case.num_kv_heads, case.head_dim)
+        if case.k_setup.shape[0]:
+            ks, vs = up16(case.k_setup), up16(case.v_setup)
+            pa.kv_append(self.geom, ks, vs, self.kp, self.vp, bt,
+                         torch.from_numpy(case.cu_setup_lens).to(dev),
+                         torch.from_numpy(case.setup_ctx_lens).to(dev))
+            del ks, vs
+        self.k_new = up16(case.k_new)
+        self.v_new = up16(case.v_new)
+        self.q_dec = up16(case.q_decode) if len(case.decode_seqs) else None
+        self.q_pre = up16(case.q_prefill) if len(case.prefill_seqs) else None
+
+
+def run_gpu(cfg: int, steps: int, warmup: int) -> dict:
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    dev = torch.device("cuda:0")
+    lib = pa.library()
+    n_layers = W.NUM_LAYERS[cfg]
+    base = W.make_case(cfg, values=False)
+    r_dec, r_pre = base.decode_seqs, base.prefill_seqs
+    bt = torch.from_numpy(base.block_tables).to(dev)
+    ctx = torch.from_numpy(base.ctx_lens).to(dev)
+    cu_new = torch.from_numpy(base.cu_new_lens).to(dev)
+    cu_q = torch.from_numpy(base.cu_q_lens_prefill).to(dev)
+    dec_bt, dec_ctx = bt[r_dec.start:r_dec.stop], ctx[r_dec.start:r_dec.stop]
+    pre_bt, pre_ctx = bt[r_pre.start:r_pre.stop], ctx[r_pre.start:r_pre.stop]
+    layers = []
+    for li in range(n_layers):
+        t0 = time.perf_counter()
+        case = W.fill_values(W.make_case(cfg, values=False), li)
+        layers.append(Layer(case, torch, pa, bt, ctx, cu_new, cu_q))
+        del case
+        torch.cuda.synchronize()
+        log(f"layer {li} resident ({time.perf_counter() - t0:.1f} s)")
+    geom = layers[0].geom
+    n_dec, n_pre = len(r_dec), len(r_pre)
+    max_ctx_dec = int(base.ctx_lens[r_dec.start:r_dec.stop].max()) if n_dec else 0
+    max_ctx_pre = int(base.ctx_lens[r_pre.start:r_pre.stop].max()) if n_pre else 0
+    max_q = int(base.q_lens_prefill.max()) if n_pre else 0
+    part = pa.decode_partition_tokens(geom, n_dec, max_ctx_dec) if n_dec else 0
+    ws_bytes = pa.decode_workspace_bytes(geom, n_dec, max_ctx_dec) if n_dec else 0
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out_dec = torch.empty((n_dec, 32, 64), dtype=torch.bfloat16, device=dev)
+    out_pre = torch.empty((int(base.q_lens_prefill.sum()), 32, 64), dtype=torch.bfloat16,
+                          device=dev)
+    stream = torch.cuda.current_stream()
+    scale = base.scale
+    n_new = int(base.new_lens.sum())
+
+    ev_dec = [] if n_dec else None
+    ev_pre = [] if n_pre else None
+    ev_app = []
+
+    def step(record: bool):
+        for L in layers:
+            if record:
+                a0 = torch.cuda.Event(enable_timing=True)
+                a0.record(stream)
+            pa.kv_append(geom, L.k_new, L.v_new, L.kp, L.vp, bt, cu_new, ctx, stream=stream)
+            if n_pre:
+                if record:
+                    p0 = torch.cuda.Event(enable_timing=True)
+                    p0.record(stream)
+                pa.prefill(geom, out_pre, L.q_pre, L.kp, L.vp, pre_bt, cu_q, pre_ctx, max_q,
+                           max_ctx_pre, scale, causal=True, stream=stream)
+            if n_dec:
+                if record:
+                    d0 = torch.cuda.Event(enable_timing=True)
+                    d0.record(stream)
+                pa.decode(geom, out_dec, L.q_dec, L.kp, L.vp, dec_bt, dec_ctx, max_ctx_dec,
+                          scale, partition_tokens=part, workspace=ws, stream=stream)
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                ev_app.append((a0, p0 if n_pre else (d0 if n_dec else e)))
+                if n_pre:
+                    ev_pre.append((p0, d0 if n_dec else e))
+                if n_dec:
+                    ev_dec.append((d0, e))
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def avg_ms(pairs):
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
+
+    ms_step = wall * 1e3 / steps
+    res = {"ms_per_step": ms_step, "n_layers": n_layers, "partition_tokens": part,
+           "append_ms": avg_ms(ev_app)}
+    kv_bytes_layer = base.kv_tokens() * KV_BYTES_PER_TOKEN
+    if n_dec:
+        dec_ms = avg_ms(ev_dec)
+        res.update(decode_ms=dec_ms, decode_bytes_per_launch=kv_bytes_layer,
+                   decode_gbps=kv_bytes_layer / (dec_ms * 1e-3) / 1e9,
+                   value=kv_bytes_layer * n_layers / (ms_step * 1e-3) / 1e9, unit="GB/s")
+    if n_pre:
+        pre_ms = avg_ms(ev_pre)
+        flops = base.prefill_pairs() * FLOP_PER_PAIR
+        res.update(prefill_ms=pre_ms, prefill_flop_per_launch=flops,
+                   prefill_tflops=flops / (pre_ms * 1e-3) / 1e12)
+        if not n_dec:
+            res.update(value=flops * n_layers / (ms_step * 1e-3) / 1e12, unit="TFLOP/s")
+    res["lib"] = os.path.basename(pa._lib.LIB_PATH)
+    del lib
+    return res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path is sharded "
+              "by sequence or KV head across GPUs with no exchange, see DESIGN.md",
+              file=sys.stderr)
+        return 2
+    cfg = WORKLOADS[args.workload]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(cfg, args.cpu_budget)
+        log(f"cpu baseline: {cpu['value']:.4f} {cpu['unit']}")
+
+    res = run_gpu(cfg, args.steps, args.warmup)
+    base = W.make_case(cfg, values=False)
+    config = {"workload": W.CONFIG_NAMES[cfg], "layers": W.NUM_LAYERS[cfg],
+              "block_size": base.block_size, "num_q_heads": 32, "num_kv_heads": 8,
+              "head_dim": 64, "decode_seqs": len(base.decode_seqs),
+              "prefill_seqs": len(base.prefill_seqs),
+              "decode_kv_tokens_per_layer": base.kv_tokens(),
+              "prefill_visible_pairs_per_layer": base.prefill_pairs(),
+              "partition_tokens": res["partition_tokens"]}
+    line = {
+        "metric": METRIC,
+        "value": round(res["value"], 2),
+        "unit": res["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/Q, shuffled pages)",
+        "config": config,
+    }
+    if "decode_ms" in res:
+        ach = res["decode_gbps"]
+        line["roofline"] = {"bound": "hbm", "kernel": "pa_decode (partition + merge)",
+                            "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "bytes_per_launch": res["decode_bytes_per_launch"],
+                            "avg_launch_ms": round(res["decode_ms"], 5)}
+    if "prefill_ms" in res:
+        ach = res["prefill_tflops"]
+        key = "roofline_prefill" if "roofline" in line else "roofline"
+        line[key] = {"bound": "mfma", "kernel": "pa_prefill", "achieved": round(ach, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flop_per_launch": res["prefill_flop_per_launch"],
+                     "avg_launch_ms": round(res["prefill_ms"], 5)}
+    line["append_ms_per_layer"] = round(res["append_ms"], 5)
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -119,12 +119,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     const float mn = fmaxf(m, mt);
     const float mref = (mn == kNegInf) ? 0.f : mn;
     const float alpha = fast_exp2(m - mref);
+    // p is rounded to bf16 once (the P.V operand); the running sum adds those same
+    // rounded values (a dot with (1, 1)), so the normaliser matches the weights used.
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      pk[i] = pack_bf16x2(fast_exp2(sv[2 * i] - mref), fast_exp2(sv[2 * i + 1] - mref));
     float ps = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sv[r] = fast_exp2(sv[r] - mref);
-      ps += sv[r];
-    }
+    for (int i = 0; i < 8; ++i) ps = dot2(pk[i], 0x3F803F80u, ps);
     lsum = lsum * alpha + ps;
     m = mn;
 #pragma unroll
@@ -136,11 +139,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     // ---- O^T += V^T . P^T ---------------------------------------------------------------
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      uint4 pb;
-      pb.x = pack_bf16x2(sv[8 * ks + 0], sv[8 * ks + 1]);
-      pb.y = pack_bf16x2(sv[8 * ks + 2], sv[8 * ks + 3]);
-      pb.z = pack_bf16x2(sv[8 * ks + 4], sv[8 * ks + 5]);
-      pb.w = pack_bf16x2(sv[8 * ks + 6], sv[8 * ks + 7]);
+      const uint4 pb = make_uint4(pk[4 * ks + 0], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]);
       const int kbase = k0 + 16 * ks;  // first key of this k-step (16 keys, one page run)
       int vpage = bt[min(kbase / BS, last_blk)];
       if ((unsigned)vpage >= (unsigned)num_pages) { bad = true; vpage = 0; }
