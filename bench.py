@@ -125,7 +125,7 @@ class Layer:
         self.q_pre = up16(case.q_prefill) if len(case.prefill_seqs) else None
 
 
-def run_gpu(cfg: int, steps: int, warmup: int) -> dict:
+def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     import torch
 
     import paged_kv_attention_31_amd as pa
@@ -154,8 +154,8 @@ def run_gpu(cfg: int, steps: int, warmup: int) -> dict:
     max_ctx_dec = int(base.ctx_lens[r_dec.start:r_dec.stop].max()) if n_dec else 0
     max_ctx_pre = int(base.ctx_lens[r_pre.start:r_pre.stop].max()) if n_pre else 0
     max_q = int(base.q_lens_prefill.max()) if n_pre else 0
-    part = pa.decode_partition_tokens(geom, n_dec, max_ctx_dec) if n_dec else 0
-    ws_bytes = pa.decode_workspace_bytes(geom, n_dec, max_ctx_dec) if n_dec else 0
+    part = pa.decode_partition_tokens(geom, n_dec, max_ctx_dec, partition) if n_dec else 0
+    ws_bytes = pa.decode_workspace_bytes(geom, n_dec, max_ctx_dec, part) if n_dec else 0
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out_dec = torch.empty((n_dec, 32, 64), dtype=torch.bfloat16, device=dev)
     out_pre = torch.empty((int(base.q_lens_prefill.sum()), 32, 64), dtype=torch.bfloat16,
@@ -229,6 +229,36 @@ def run_gpu(cfg: int, steps: int, warmup: int) -> dict:
     return res
 
 
+def copy_calibration(nbytes: int, reps: int) -> dict:
+    """Device-to-device copy of ``nbytes`` (torch's copy kernel), timed with HIP events.
+
+    Gives the box's achievable HBM bandwidth as context, and a kernel whose HBM traffic
+    is known exactly (nbytes read + nbytes written per launch), against which the
+    rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    n = nbytes // 2
+    a = torch.empty(n, dtype=torch.int16, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ms = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    avg = float(np.mean(ms[1:] if len(ms) > 1 else ms))
+    return {"kind": "hbm-copy", "bytes_read": 2 * n, "bytes_written": 2 * n, "reps": reps,
+            "avg_ms": round(avg, 5),
+            "gbps_read_plus_write": round(4 * n / (avg * 1e-3) / 1e9, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,12 +267,20 @@ def main() -> int:
     ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--partition", type=int, default=0,
+                    help="decode KV tokens per split-K partition (0 = the library's choice)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the workload, time a device copy of this many bytes "
+                         "(HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path is sharded "
-              "by sequence or KV head across GPUs with no exchange, see DESIGN.md",
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+              "multi-GPU path; the attention shards by sequence or KV head with no exchange",
               file=sys.stderr)
         return 2
+    if args.copy_bytes > 0:
+        print(json.dumps(copy_calibration(args.copy_bytes, max(2, args.steps))), flush=True)
+        return 0
     cfg = WORKLOADS[args.workload]
 
     cpu = None
@@ -251,7 +289,7 @@ def main() -> int:
         cpu = cpu_baseline(cfg, args.cpu_budget)
         log(f"cpu baseline: {cpu['value']:.4f} {cpu['unit']}")
 
-    res = run_gpu(cfg, args.steps, args.warmup)
+    res = run_gpu(cfg, args.steps, args.warmup, args.partition)
     base = W.make_case(cfg, values=False)
     config = {"workload": W.CONFIG_NAMES[cfg], "layers": W.NUM_LAYERS[cfg],
               "block_size": base.block_size, "num_q_heads": 32, "num_kv_heads": 8,

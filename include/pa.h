@@ -145,20 +145,33 @@ int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool
 /* ---------------------------------------------------------------------------------
  * Decode ([guide] §推理流程, §在线Softmax): one query row per sequence, the newest
  * token at position ctx_lens[s]-1, attending to all ctx_lens[s] keys (so the token's
- * own K/V must already be appended).  For each (sequence, KV head) the kernel streams
- * the sequence's pages once for all query heads of the group, keeping a running max
- * and running sum per head; with more than one KV partition the partial results
- * (max, sum, unnormalised output; fp32) go to `workspace` and a second kernel merges
- * them by log-sum-exp.
+ * own K/V must already be appended).  Every (sequence, KV head) pair is streamed once
+ * for all query heads of its group with a running max and running sum per head.
+ * The work is cut evenly over "workers": the (sequence, KV head) pairs, each a run of
+ * ceil(ctx/64) tiles of 64 tokens, are laid end to end and every worker takes an equal
+ * contiguous share of tiles, so a pair may be split between workers; each worker then
+ * leaves an fp32 partial (max, sum, unnormalised output) in `workspace` and a second
+ * kernel merges the partials of split pairs by log-sum-exp in a fixed order.
  *   out, q          [n_seqs][num_q_heads][head_dim] bf16 (device)
- *   ctx_lens        int32 [n_seqs] (device); 0 gives a zero row
- *   max_ctx_len     host upper bound of ctx_lens (1 <= max_ctx_len <=
- *                   max_blocks_per_seq * block_size); it sizes the grid
+ *   ctx_lens        int32 [n_seqs] (device); 0 gives a zero row; values above
+ *                   max_ctx_len are treated as max_ctx_len
+ *   max_ctx_len     host upper bound of ctx_lens (0 <= max_ctx_len <=
+ *                   max_blocks_per_seq * block_size); with n_seqs it bounds the work
+ *                   (n_seqs * num_kv_heads * ceil(max_ctx_len/64) < 2^31)
  *   scale           multiplies q.k before the softmax (1/sqrt(head_dim) = 0.125)
- *   partition_tokens  KV tokens per partition: 0 = choose automatically, else a
- *                   positive multiple of 256
+ *   partition_tokens  0: four workers per compute unit of the current device; else a
+ *                   positive multiple of 64, and enough workers that none streams more
+ *                   than that many tokens.  Either way no worker takes more than
+ *                   56 * num_kv_heads tiles.  Other values give PA_ERR_INVALID_ARG.
  *   workspace       device scratch of at least pa_decode_workspace_bytes(...) bytes
- *                   for the same arguments; may be NULL when that size is 0
+ *                   for the same arguments (on the same device); may be NULL when that
+ *                   size is 0.  With W workers and S = n_seqs * num_kv_heads + W it is
+ *                   S * 4 * (64 * 4 + 8) + 8 * W bytes (fp32 partials, then two int32
+ *                   lists of W), or 0 when no pair can be split (ceil(max_ctx_len/64) <= 1
+ *                   or W = 1).  Its contents need no initialisation and are scratch
+ *                   after the call; concurrent calls need separate workspaces.
+ * pa_decode_partition_tokens returns the most tokens one worker streams for these
+ * arguments (a multiple of 64), or a negative status.
  * ------------------------------------------------------------------------------- */
 int32_t pa_decode_partition_tokens(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,
                                    int32_t partition_tokens);

@@ -28,24 +28,31 @@ pa::LaunchGeom to_launch(const pa_geom_t& g) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tokens per decode partition.  Explicit values are kept (validated by the caller);
-// otherwise split so that (sequences x KV heads x partitions) gives the chip enough
-// workgroups (256 CUs, several resident workgroups each) without making partitions so
-// short that the merge traffic matters.
-int32_t choose_partition(const pa_geom_t& g, int32_t n_seqs, int32_t max_ctx_len,
-                         int32_t requested) {
-  const int32_t q = pa::kDecodePartQuantum;
-  const int64_t quanta = std::max<int64_t>(1, ceil_div(std::max(max_ctx_len, 1), q));
-  if (requested > 0) return requested;
-  const int64_t units = std::max<int64_t>(1, (int64_t)n_seqs * g.num_kv_heads);
-  constexpr int64_t kTargetBlocks = 4096;
-  int64_t f = std::max<int64_t>(1, (units * quanta) / kTargetBlocks);
-  f = std::min(f, quanta);
-  return (int32_t)(f * q);
+// Compute units of the current device (the automatic decode plan uses four workers per
+// unit); 256 (MI355X) when no device can be queried.
+int compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  return cus;
 }
 
-int32_t num_parts(int32_t max_ctx_len, int32_t part) {
-  return (int32_t)std::max<int64_t>(1, ceil_div(std::max(max_ctx_len, 0), part));
+bool partition_ok(int32_t partition_tokens) {
+  return partition_tokens >= 0 && partition_tokens % 64 == 0;
+}
+
+// Host-checkable decode arguments shared by the sizing and launch entry points.
+int decode_args_ok(const pa_geom_t& g, int32_t n_seqs, int32_t max_ctx_len,
+                   int32_t partition_tokens) {
+  int st = pa_geom_check(g);
+  if (st != PA_OK) return st;
+  if (n_seqs < 0 || max_ctx_len < 0 || !partition_ok(partition_tokens)) return PA_ERR_INVALID_ARG;
+  // the tile stream is counted in int32 on the device
+  const int64_t tiles = std::max<int64_t>(1, ceil_div(max_ctx_len, 64));
+  if ((int64_t)n_seqs * tiles * g.num_kv_heads > (int64_t)INT32_MAX) return PA_ERR_INVALID_ARG;
+  return PA_OK;
 }
 
 }  // namespace
@@ -188,39 +195,37 @@ int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool
 
 int32_t pa_decode_partition_tokens(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,
                                    int32_t partition_tokens) {
-  if (pa_geom_check(g) != PA_OK || n_seqs < 0 || max_ctx_len < 0) return PA_ERR_INVALID_ARG;
-  if (partition_tokens < 0 || partition_tokens % pa::kDecodePartQuantum != 0)
-    return PA_ERR_INVALID_ARG;
-  return choose_partition(g, n_seqs, max_ctx_len, partition_tokens);
+  const int st = decode_args_ok(g, n_seqs, max_ctx_len, partition_tokens);
+  if (st != PA_OK) return st;
+  const pa::DecodePlan p = pa::plan_decode(n_seqs, max_ctx_len, g.num_kv_heads, partition_tokens,
+                                           compute_units());
+  return (int32_t)std::min<int64_t>(p.tiles_per_worker * 64, INT32_MAX);
 }
 
 size_t pa_decode_workspace_bytes(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,
                                  int32_t partition_tokens) {
-  const int32_t part = pa_decode_partition_tokens(g, n_seqs, max_ctx_len, partition_tokens);
-  if (part <= 0) return 0;
-  return pa::decode_workspace_bytes(n_seqs, num_parts(max_ctx_len, part), g.num_q_heads);
+  if (decode_args_ok(g, n_seqs, max_ctx_len, partition_tokens) != PA_OK) return 0;
+  return pa::plan_decode(n_seqs, max_ctx_len, g.num_kv_heads, partition_tokens, compute_units())
+      .ws_bytes;
 }
 
 int pa_decode(pa_geom_t g, void* out, const void* q, const void* k_pool, const void* v_pool,
               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* ctx_lens,
               int32_t n_seqs, int32_t max_ctx_len, float scale, int32_t partition_tokens,
               void* workspace, size_t workspace_bytes, void* stream) {
-  int st = pa_geom_check(g);
+  const int st = decode_args_ok(g, n_seqs, max_ctx_len, partition_tokens);
   if (st != PA_OK) return st;
-  if (n_seqs < 0 || max_blocks_per_seq <= 0 || max_ctx_len < 0) return PA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
   if ((int64_t)max_ctx_len > (int64_t)max_blocks_per_seq * g.block_size) return PA_ERR_INVALID_ARG;
-  if (partition_tokens < 0 || partition_tokens % pa::kDecodePartQuantum != 0)
-    return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (n_seqs == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !ctx_lens) return PA_ERR_INVALID_ARG;
-  const int32_t part = choose_partition(g, n_seqs, max_ctx_len, partition_tokens);
-  const int32_t np = num_parts(max_ctx_len, part);
-  if ((int64_t)n_seqs * g.num_kv_heads * np > (int64_t)INT32_MAX) return PA_ERR_INVALID_ARG;
-  const size_t need = pa::decode_workspace_bytes(n_seqs, np, g.num_q_heads);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
-  return hip_status(pa::launch_decode(to_launch(g), out, q, k_pool, v_pool, block_tables,
-                                      max_blocks_per_seq, ctx_lens, n_seqs, np, part, scale,
+  const pa::DecodePlan plan = pa::plan_decode(n_seqs, max_ctx_len, g.num_kv_heads,
+                                              partition_tokens, compute_units());
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return PA_ERR_WORKSPACE;
+  return hip_status(pa::launch_decode(to_launch(g), plan, out, q, k_pool, v_pool, block_tables,
+                                      max_blocks_per_seq, ctx_lens, n_seqs, max_ctx_len, scale,
                                       workspace, static_cast<hipStream_t>(stream)));
 }
 

@@ -5,29 +5,39 @@
 // block table, and softmax runs in one pass with a running maximum and a running sum
 // that is rescaled whenever the maximum grows.  Decode moves every KV byte once and
 // does 4 flop per byte, so the kernel is bound by HBM bandwidth (same guide,
-// §推理流程: decode is memory-bound); everything below is arranged around streaming
-// the pages with wide coalesced loads.
+// §推理流程: decode is memory-bound); everything below is arranged around keeping the
+// HBM pipe full.
 //
-// Work split: one workgroup (4 waves) per (sequence, KV head, KV partition).  The four
-// query heads of the KV head share every K/V byte the workgroup reads.  A wave takes
-// 64-token tiles of the partition (tiles w, w+4, ...):
-//   scores:  lane t owns token t of the tile.  The K page layout [Hkv][8][bs][8] makes
-//            "lane t reads piece c of token t" a contiguous run over lanes, so eight
-//            16-byte loads per lane bring the lane its token's whole K row.  q (4 heads,
-//            bf16) sits in LDS and is read as 16-byte broadcasts; dot products use
-//            v_dot2c_f32_bf16 (two bf16 products per instruction, fp32 accumulate).
+// Work split (stream-K).  Every (sequence s, KV head g) pair is a segment of
+// tiles(ctx_s) = ceil(ctx_s / 64) tiles of 64 tokens (an empty context counts one empty
+// tile).  Segments are laid end to end in (s, g) order and the whole tile stream is cut
+// into equal contiguous ranges, one per worker wave, so every wave moves the same
+// number of bytes whatever the length mix.  The prefix sum over the context lengths
+// that this needs is computed on the device by every workgroup (the lengths never go to
+// the host).  A wave streams its range tile by tile, crossing segment boundaries
+// without a pause: the K/V loads of the next tile and the page ids and q of the tile
+// after it are in flight while the current tile is computed.  The four query heads of
+// a KV head share every K/V byte read.
+//
+// Per tile (wave-local, no workgroup barrier):
+//   scores:  lane t owns token t.  The K page layout [Hkv][8][bs][8] makes "lane t reads
+//            piece c of token t" a contiguous run over lanes, so eight 16-byte loads per
+//            lane bring the lane its token's whole K row.  q (4 heads, bf16) sits in LDS
+//            and is read as 16-byte broadcasts; dot products use v_dot2c_f32_bf16 (two
+//            bf16 products per instruction, fp32 accumulate).
 //   softmax: per head a wave max (DPP inside 16-lane rows, readlane across rows), scores
 //            pre-scaled by scale*log2(e) so exponentials are exp2; the probabilities are
 //            rounded to bf16 and go to LDS.
 //   P.V:     the V page layout [Hkv][64][bs] gives each lane 8 consecutive tokens of one
 //            dimension per 16-byte load, i.e. bf16 pairs along the token axis, so P.V is
-//            again v_dot2c_f32_bf16 (fp32 accumulate) against the lane's 8 probabilities.  Tokens past the end of the context are excluded
-//            by selection, never by multiplying by a zero weight, so stale pool bytes
-//            (even NaN) cannot leak.
-// At the end the 4 waves merge their (max, sum, output) through LDS.  With one
-// partition the workgroup writes the normalised bf16 row; otherwise it writes fp32
-// partials and decode_merge_kernel combines partitions in ascending order (fixed order:
-// results do not depend on scheduling).
+//            again v_dot2c_f32_bf16 against the lane's 8 probabilities.  Tokens past the
+//            end of the context are excluded by selection, never by multiplying by a
+//            zero weight, so stale pool bytes (even NaN) cannot leak.
+// A segment that lies wholly inside one wave's range is normalised and written as bf16
+// by that wave.  A segment cut by range boundaries leaves one fp32 partial (running max,
+// running sum, unnormalised output) per wave that touched it, and decode_merge_kernel
+// combines them by log-sum-exp in ascending wave order (a fixed order: results do not
+// depend on scheduling).
 #include <algorithm>
 
 #include "common.h"
@@ -37,117 +47,229 @@ namespace pa {
 
 namespace {
 
+constexpr int kTile = 64;  // tokens per tile: one per lane for the scores
+
+__device__ __forceinline__ int tiles_of(int ctx) { return ctx > 0 ? (ctx + kTile - 1) / kTile : 1; }
+
+__device__ __forceinline__ int readlane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+// A position in a wave's tile stream (wave-uniform values).
+struct Cursor {
+  int s;    // sequence
+  int g;    // KV head
+  int i;    // tile within the (s, g) segment
+  int ctx;  // context length of s (clamped)
+  int nt;   // tiles per KV head of s
+};
+
+// K and V registers of one tile: lane t holds the K row of token t; for V, the lane holds
+// 8 consecutive tokens of NV head dimensions of each of the PPT pages of the tile.
 template <int BS>
-__global__ __launch_bounds__(256) void decode_part_kernel(
+struct DecodeTile {
+  static constexpr int PPT = kTile / BS;  // pages per tile
+  static constexpr int NV = BS / 8;       // 16-byte V loads per page (= dims per lane)
+  uint4 k[8];
+  uint4 v[PPT][NV];
+};
+
+template <int BS>
+__global__ __launch_bounds__(256) void decode_stream_kernel(
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
+    int* __restrict__ ws_seg, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
-    int max_blocks, const int32_t* __restrict__ ctx_lens, int num_pages, int num_kv_heads,
-    int n_parts, int part_tokens, float qk_scale) {
+    int max_blocks, const int32_t* __restrict__ ctx_lens, int n_seqs, int ctx_cap,
+    int num_pages, int num_kv_heads, int n_workers, float qk_scale) {
+  using Tile = DecodeTile<BS>;
+  constexpr int PPT = Tile::PPT;
+  constexpr int NV = Tile::NV;
   constexpr int LPR = BS / 8;    // lanes sharing one V row (one head dimension)
   constexpr int RPI = 64 / LPR;  // V rows covered by one 16-byte-per-lane load
-  constexpr int PPT = 64 / BS;   // pages per 64-token tile
-  constexpr int NV = LPR;        // head dimensions each lane accumulates
 
-  const int bid = blockIdx.x;
-  const int part = bid % n_parts;
-  const int sg = bid / n_parts;
-  const int g = sg % num_kv_heads;
-  const int s = sg / num_kv_heads;
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
-  const int hq = num_kv_heads * kGroup;
+  const int hkv = num_kv_heads;
+  const int hq = hkv * kGroup;
 
-  int ctx = ctx_lens[s];
-  ctx = max(0, min(min(ctx, max_blocks * BS), n_parts * part_tokens));
-  const int p0 = part * part_tokens;
-  const int p1 = min(ctx, p0 + part_tokens);
-  if (n_parts > 1 && p0 >= ctx) return;  // partition past the end: the merge skips it
+  __shared__ int scan_sh[257];
+  __shared__ int wsum_sh[kDecodeWaves];
+  __shared__ uint4 q_sh[kDecodeWaves][2][kGroup][8];  // [wave][slot][head][piece]
+  __shared__ __attribute__((aligned(16))) uint16_t p_sh[kDecodeWaves][kGroup][64];
 
-  __shared__ uint4 q_sh[kGroup][8];                // [head][piece], bf16 x 8
-  __shared__ __attribute__((aligned(16))) uint16_t p_sh[kDecodeWaves][kGroup][64];  // bf16 p
-  __shared__ float red_m[kDecodeWaves][kGroup];
-  __shared__ float red_l[kDecodeWaves][kGroup];
-  __shared__ float red_o[kDecodeWaves][kGroup][64];
-  __shared__ int bad_sh;
-
-  if (tid < kGroup * 8) {
-    q_sh[tid >> 3][tid & 7] =
-        reinterpret_cast<const uint4*>(q + ((size_t)s * hq + g * kGroup) * kHeadDim)[tid];
+  // ---- 1. tiles per sequence and their exclusive prefix sum over 256 chunks -----------
+  const int chunk = (n_seqs + 255) / 256;
+  int mine = 0;
+  for (int j = 0; j < chunk; ++j) {
+    const int s = tid * chunk + j;
+    if (s < n_seqs) mine += tiles_of(min(max(ctx_lens[s], 0), ctx_cap));
   }
-  if (tid == 0) bad_sh = 0;
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum_sh[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int v = 0; v < w; ++v) before += wsum_sh[v];
+  scan_sh[tid] = before + incl - mine;
+  if (tid == 255) scan_sh[256] = before + incl;
   __syncthreads();
 
-  const int32_t* bt = block_tables + (size_t)s * max_blocks;
-  const size_t head_stride = (size_t)kHeadDim * BS;  // elements of one (page, head)
-  const size_t page_stride = head_stride * num_kv_heads;
-  const uint16_t* k_head = k_pool + g * head_stride;
-  const uint16_t* v_head = v_pool + g * head_stride + (lane / LPR) * BS + (lane % LPR) * 8;
-
-  float m[kGroup], l[kGroup], acc[NV][kGroup];
-#pragma unroll
-  for (int h = 0; h < kGroup; ++h) {
-    m[h] = kNegInf;
-    l[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) acc[i][h] = 0.f;
+  // ---- 2. this wave's range [a, b) of the tile stream ---------------------------------
+  const int wid = blockIdx.x * kDecodeWaves + w;
+  if (wid >= n_workers) return;  // no workgroup barrier follows
+  const bool has_ws = ws_seg != nullptr;
+  const int64_t n_tiles = (int64_t)scan_sh[256] * hkv;
+  const int64_t n_eff = min((int64_t)n_workers, n_tiles);
+  if (wid >= n_eff) {
+    if (has_ws && lane == 0) {
+      ws_seg[wid] = -1;
+      ws_seg[n_workers + wid] = -1;
+    }
+    return;
   }
-  int bad = 0;
+  const int64_t a = (int64_t)wid * n_tiles / n_eff;
+  const int L = (int)((int64_t)(wid + 1) * n_tiles / n_eff - a);
 
-  const int n_tiles = p1 > p0 ? (p1 - p0 + 63) / 64 : 0;
-  for (int ti = w; ti < n_tiles; ti += kDecodeWaves) {
-    const int t0 = p0 + ti * 64;
-    const int nvalid = min(64, p1 - t0);
-    const int last_blk = (p1 - 1) / BS;
-
-    // ---- K: lane owns one token --------------------------------------------------------
-    const int pos = t0 + min(lane, nvalid - 1);
-    int kpage = bt[pos / BS];
-    if ((unsigned)kpage >= (unsigned)num_pages) { bad = 1; kpage = 0; }
-    const uint16_t* kb = k_head + (size_t)kpage * page_stride + (pos % BS) * 8;
-    uint4 kc[8];
+  // chunk holding tile a, then the sequence inside it (64 sequences per step)
+  int lo = 0, hi = 255;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)scan_sh[mid] * hkv <= a) lo = mid; else hi = mid - 1;
+  }
+  Cursor cc{-1, 0, 0, 0, 1};
+  int64_t cum = scan_sh[lo];
+  for (int s0 = lo * chunk; s0 < n_seqs; s0 += 64) {
+    const int sj = s0 + lane;
+    const int cj = sj < n_seqs ? min(max(ctx_lens[sj], 0), ctx_cap) : 0;
+    const int nj = sj < n_seqs ? tiles_of(cj) : 0;
+    int pre = nj;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kc[c] = *reinterpret_cast<const uint4*>(kb + c * BS * 8);
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(pre, off, kWave);
+      if (lane >= off) pre += y;
+    }
+    const uint64_t hit = __ballot(a < (int64_t)hkv * (cum + pre));
+    if (hit) {
+      const int j = __ffsll((unsigned long long)hit) - 1;
+      cc.s = s0 + j;
+      cc.ctx = readlane_i(cj, j);
+      cc.nt = readlane_i(nj, j);
+      cum += readlane_i(pre - nj, j);
+      break;
+    }
+    cum += readlane_i(pre, 63);
+  }
+  if (cc.s < 0) return;  // unreachable: tile a < n_tiles lies in some sequence
+  {
+    const int off = (int)(a - (int64_t)hkv * cum);
+    cc.g = off / cc.nt;
+    cc.i = off - cc.g * cc.nt;
+  }
+  // Context lengths of the next 64 sequences, one per lane.  A range is at most 56 * Hkv
+  // tiles long (the host sizes the worker count for that) and every sequence holds at
+  // least Hkv tiles, so a range touches at most 58 sequences.
+  const int cache_base = cc.s;
+  const int cache_ctx =
+      cache_base + lane < n_seqs ? min(max(ctx_lens[cache_base + lane], 0), ctx_cap) : 0;
+  auto advance = [&](Cursor& c) {
+    if (++c.i == c.nt) {
+      c.i = 0;
+      if (++c.g == hkv) {
+        c.g = 0;
+        ++c.s;
+        c.ctx = readlane_i(cache_ctx, min(c.s - cache_base, 63));
+        c.nt = tiles_of(c.ctx);
+      }
+    }
+  };
 
-    // ---- V: lane owns 8 consecutive tokens of NV dimensions, per page ----------------
-    uint4 vc[PPT][NV];
+  const size_t head_stride = (size_t)kHeadDim * BS;  // elements of one (page, head)
+  const size_t page_stride = head_stride * hkv;
+
+  // page ids of a tile: lane l reads the entry of page (l % PPT) of the tile; pages past
+  // the last block of the context repeat the last block (never read as data)
+  auto load_pages = [&](const Cursor& c) -> int {
+    const int last = c.ctx > 0 ? (c.ctx - 1) / BS : 0;
+    const int blk = min(c.i * PPT + lane % PPT, last);
+    return block_tables[(size_t)c.s * max_blocks + blk];
+  };
+  // q of the tile's segment: lane l (and l + 32) reads piece l % 8 of head (l % 32) / 8
+  auto load_q = [&](const Cursor& c) -> uint4 {
+    return reinterpret_cast<const uint4*>(q + ((size_t)c.s * hq + c.g * kGroup) * kHeadDim)
+        [lane & 31];
+  };
+  auto store_q = [&](int slot, uint4 v) {
+    if (lane < 32) q_sh[w][slot][lane >> 3][lane & 7] = v;
+  };
+  // Issue the K/V loads of a tile.  `live` false (a tile past the end of the range)
+  // points every lane at one 16-byte piece, so each load instruction fetches one line.
+  // Returns true if a page id is out of range (page 0 is read instead).
+  auto load_kv = [&](Tile& t, const Cursor& c, int pid, bool live) -> bool {
+    int pg[PPT];
+    bool bad = false;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-      int vpage = bt[min(t0 / BS + j, last_blk)];
-      if ((unsigned)vpage >= (unsigned)num_pages) { bad = 1; vpage = 0; }
-      const uint16_t* vb = v_head + (size_t)vpage * page_stride;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) vc[j][i] = *reinterpret_cast<const uint4*>(vb + i * RPI * BS);
+      pg[j] = readlane_i(pid, j);
+      if (c.ctx == 0) pg[j] = 0;  // an empty context has no pages to name
+      if ((unsigned)pg[j] >= (unsigned)num_pages) {
+        bad = true;
+        pg[j] = 0;
+      }
     }
+    int kpage = pg[0];
+#pragma unroll
+    for (int j = 1; j < PPT; ++j) kpage = (live && lane >= j * BS) ? pg[j] : kpage;
+    const size_t hoff = (size_t)c.g * head_stride;
+    const uint16_t* kb = k_pool + (size_t)kpage * page_stride + hoff + (live ? (lane % BS) * 8 : 0);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) t.k[p] = *reinterpret_cast<const uint4*>(kb + p * BS * 8);
+    const int vl = live ? (lane / LPR) * BS + (lane % LPR) * 8 : 0;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const uint16_t* vb = v_pool + (size_t)pg[j] * page_stride + hoff + vl;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) t.v[j][i] = *reinterpret_cast<const uint4*>(vb + i * RPI * BS);
+    }
+    return bad;
+  };
 
-    // ---- scores ------------------------------------------------------------------------
-    // q is re-read from LDS every tile as 16-byte broadcasts, one piece ahead of its use;
-    // the opaque zero offset and the scheduling fences keep the compiler from hoisting
-    // all 32 reads (128 registers) out of the loop.
+  float m[kGroup], l[kGroup], acc[NV][kGroup];
+  auto reset = [&]() {
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      m[h] = kNegInf;
+      l[h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i][h] = 0.f;
+    }
+  };
+  reset();
+
+  // scores, online-softmax update and P.V of the tile at cursor c, held in t
+  auto compute = [&](const Tile& t, const Cursor& c, int slot) {
+    const int nvalid = min(max(c.ctx - c.i * kTile, 0), kTile);
+    // q is re-read from LDS every tile as 16-byte broadcasts, one piece at a time; the
+    // opaque zero offset and the scheduling fences keep the compiler from hoisting all
+    // 32 reads (128 registers) out of the loop.
     int qofs = 0;
     asm volatile("" : "+s"(qofs));
-    const uint4* qrow = &q_sh[0][0] + qofs;
+    const uint4* qrow = &q_sh[w][slot][0][0] + qofs;
     float x[kGroup] = {0.f, 0.f, 0.f, 0.f};
-    uint4 qn[kGroup];
 #pragma unroll
-    for (int h = 0; h < kGroup; ++h) qn[h] = qrow[h * 8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int p = 0; p < 8; ++p) {
       uint4 qc[kGroup];
 #pragma unroll
-      for (int h = 0; h < kGroup; ++h) qc[h] = qn[h];
-      if (c + 1 < 8) {
-#pragma unroll
-        for (int h = 0; h < kGroup; ++h) qn[h] = qrow[h * 8 + c + 1];
-      }
+      for (int h = 0; h < kGroup; ++h) qc[h] = qrow[h * 8 + p];
 #pragma unroll
       for (int h = 0; h < kGroup; ++h) {
         float a = x[h];
-        a = dot2(kc[c].x, qc[h].x, a);
-        a = dot2(kc[c].y, qc[h].y, a);
-        a = dot2(kc[c].z, qc[h].z, a);
-        a = dot2(kc[c].w, qc[h].w, a);
+        a = dot2(t.k[p].x, qc[h].x, a);
+        a = dot2(t.k[p].y, qc[h].y, a);
+        a = dot2(t.k[p].z, qc[h].z, a);
+        a = dot2(t.k[p].w, qc[h].w, a);
         x[h] = a;
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -155,15 +277,14 @@ __global__ __launch_bounds__(256) void decode_part_kernel(
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) x[h] = lane < nvalid ? x[h] * qk_scale : kNegInf;
 
-    // ---- online softmax update ---------------------------------------------------------
     // p is rounded to bf16 once; the same rounded value feeds both the running sum and
     // the P.V product, so the output is an exact convex combination of the V rows.
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
-      const float mt = wave_max(x[h]);
-      const float mn = fmaxf(m[h], mt);
-      const float alpha = fast_exp2(m[h] - mn);  // 0 on the first tile (m = -inf)
-      const uint16_t pb = to_bf16(fast_exp2(x[h] - mn));  // 0 for tokens past the end
+      const float mn = fmaxf(m[h], wave_max(x[h]));
+      const float mref = mn == kNegInf ? 0.f : mn;  // a tile with no key keeps m = -inf
+      const float alpha = fast_exp2(m[h] - mref);   // 0 while m = -inf
+      const uint16_t pb = to_bf16(fast_exp2(x[h] - mref));  // 0 for tokens past the end
       l[h] = l[h] * alpha + __uint_as_float((uint32_t)pb << 16);
       m[h] = mn;
 #pragma unroll
@@ -174,7 +295,6 @@ __global__ __launch_bounds__(256) void decode_part_kernel(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- P.V: two tokens per v_dot2c_f32_bf16 -------------------------------------------
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int tb = j * BS + (lane % LPR) * 8;  // tile index of this lane's first token
@@ -183,8 +303,8 @@ __global__ __launch_bounds__(256) void decode_part_kernel(
       for (int h = 0; h < kGroup; ++h) pp[h] = *reinterpret_cast<const uint4*>(&p_sh[w][h][tb]);
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        uint4 vv = vc[j][i];
-        if (nvalid < 64) {
+        uint4 vv = t.v[j][i];
+        if (nvalid < kTile) {
           // tokens past the end may hold stale bytes (even NaN): clear them
           uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -207,136 +327,227 @@ __global__ __launch_bounds__(256) void decode_part_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
+  };
 
-  // ---- merge lanes, then waves -------------------------------------------------------------
-#pragma unroll
-  for (int h = 0; h < kGroup; ++h) {
-    l[h] = wave_sum(l[h]);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      float a = acc[i][h];
-      a += shfl_xor_f(a, 1);
-      if (LPR == 4) a += shfl_xor_f(a, 2);
-      acc[i][h] = a;
-    }
-  }
-  if (lane % LPR == 0) {
+  // End of a segment's part in this range: the bf16 output if the whole segment was
+  // here, else an fp32 partial in slot (s * Hkv + g) + wid.
+  auto finish = [&](const Cursor& c, bool whole, bool bad) {
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
+      l[h] = wave_sum(l[h]);
 #pragma unroll
-      for (int i = 0; i < NV; ++i) red_o[w][h][i * RPI + lane / LPR] = acc[i][h];
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < kGroup; ++h) {
-      red_m[w][h] = m[h];
-      red_l[w][h] = l[h];
-    }
-  }
-  if (bad) bad_sh = 1;
-  __syncthreads();
-
-  const int h = tid >> 6;
-  const int d = tid & 63;
-  float M = kNegInf;
-#pragma unroll
-  for (int v = 0; v < kDecodeWaves; ++v) M = fmaxf(M, red_m[v][h]);
-  float L = 0.f, O = 0.f;
-  if (M != kNegInf) {
-#pragma unroll
-    for (int v = 0; v < kDecodeWaves; ++v) {
-      const float mv = red_m[v][h];
-      if (mv != kNegInf) {
-        const float f = fast_exp2(mv - M);
-        L += red_l[v][h] * f;
-        O += red_o[v][h][d] * f;
+      for (int i = 0; i < NV; ++i) {
+        float a = acc[i][h];
+        a += shfl_xor_f(a, 1);
+        if (LPR == 4) a += shfl_xor_f(a, 2);
+        acc[i][h] = bad ? __builtin_nanf("") : a;
       }
     }
+    const int seg = c.s * hkv + c.g;
+    if (whole) {
+      if (lane % LPR == 0) {
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) {
+          const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
+          uint16_t* o = out + ((size_t)c.s * hq + c.g * kGroup + h) * kHeadDim + lane / LPR;
+#pragma unroll
+          for (int i = 0; i < NV; ++i) o[i * RPI] = to_bf16(acc[i][h] * inv);
+        }
+      }
+    } else {
+      const size_t slot = (size_t)seg + wid;
+      if (lane % LPR == 0) {
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) {
+          float* o = ws_o + (slot * kGroup + h) * kHeadDim + lane / LPR;
+#pragma unroll
+          for (int i = 0; i < NV; ++i) o[i * RPI] = acc[i][h];
+        }
+      }
+      if (lane < kGroup) {
+        float mv = m[0], lv = l[0];
+#pragma unroll
+        for (int h = 1; h < kGroup; ++h) {
+          mv = lane == h ? m[h] : mv;
+          lv = lane == h ? l[h] : lv;
+        }
+        ws_ml[slot * kGroup + lane] = make_float2(mv, lv);
+      }
+    }
+    reset();
+  };
+
+  // ---- 3. stream the range ------------------------------------------------------------
+  // Cursors: cc is the tile computed now, c1 the tile whose K/V loads go out now, c2 the
+  // tile whose page ids and q go out now.  Past the end of the range c1 and c2 stay on
+  // the last tile and their loads are the cheap `live = false` kind.
+  const int seg_first = cc.s * hkv + cc.g;
+  bool seg_whole = cc.i == 0;  // this range holds the segment's first tile
+  bool seg_bad = false;
+  Cursor c1, c2;
+
+  // The prologue issues its loads in the order a pipeline step does (page ids and q of
+  // the tile after next, then K/V of the next tile), and the loop is unrolled by two with
+  // fixed registers per parity, so the compiler's wait counts keep one tile in flight
+  // behind the one being computed.
+  Tile ta, tb;
+  bool bad_a = false, bad_b = false;
+  int pid_x, pid_y;   // page ids: x for odd tiles, y for even tiles (after the first)
+  uint4 q_x, q_y;
+  {
+    const int pid0 = load_pages(cc);
+    store_q(0, load_q(cc));
+    Cursor c0 = cc;
+    c1 = cc;
+    if (L > 1) advance(c1);
+    pid_x = load_pages(c1);
+    q_x = load_q(c1);
+    bad_a = load_kv(ta, c0, pid0, true);
   }
-  if (bad_sh) O = __builtin_nanf("");
-  const int head = g * kGroup + h;
-  if (n_parts == 1) {
-    out[((size_t)s * hq + head) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : O * 0.f);
-  } else {
-    const size_t slot = ((size_t)s * n_parts + part) * hq + head;
-    ws_o[slot * kHeadDim + d] = O;
-    if (d == 0) ws_ml[slot] = make_float2(M, L);
+  c2 = c1;
+  if (L > 2) advance(c2);
+
+  // one pipeline step: compute tile t (buffer cur); load K/V of tile t+1 (buffer nxt,
+  // page ids pid_n1, q q_n1 already loaded); load page ids and q of tile t+2
+  auto step = [&](Tile& cur, bool& bad_cur, Tile& nxt, bool& bad_nxt, int& pid_n1, int& pid_n2,
+                  uint4& q_n1, uint4& q_n2, int t) {
+    pid_n2 = load_pages(c2);
+    q_n2 = load_q(c2);
+    bad_nxt = load_kv(nxt, c1, pid_n1, t + 1 < L);
+    seg_bad |= bad_cur;
+    compute(cur, cc, t & 1);
+    if (t == L - 1 || cc.i == cc.nt - 1) {
+      finish(cc, seg_whole && cc.i == cc.nt - 1, seg_bad);
+      seg_whole = true;
+      seg_bad = false;
+    }
+    store_q((t + 1) & 1, q_n1);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    cc = c1;
+    c1 = c2;
+    if (t + 3 < L) advance(c2);
+  };
+  int last_seg = seg_first;
+  for (int t = 0; t < L; t += 2) {
+    last_seg = cc.s * hkv + cc.g;
+    step(ta, bad_a, tb, bad_b, pid_x, pid_y, q_x, q_y, t);
+    if (t + 1 >= L) break;
+    last_seg = cc.s * hkv + cc.g;
+    step(tb, bad_b, ta, bad_a, pid_y, pid_x, q_y, q_x, t + 1);
+  }
+  if (has_ws && lane == 0) {
+    ws_seg[wid] = seg_first;
+    ws_seg[n_workers + wid] = last_seg;
   }
 }
 
-// Combine partition partials of one (sequence, KV head): M = max_j m_j,
-// L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L, j ascending.
+// Combine the partials of every segment that range boundaries cut.  Wave wid owns the
+// segment its range ends in if that segment continues into range wid + 1 and did not
+// start in range wid - 1; it merges the partials of waves wid, wid + 1, ... (slots
+// seg + wave) in that order: M = max_j m_j, L = sum_j l_j 2^(m_j - M),
+// out = sum_j o_j 2^(m_j - M) / L.  Lane = head dimension.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
-    const int32_t* __restrict__ ctx_lens, int max_tokens, int num_kv_heads, int n_parts,
-    int part_tokens) {
-  const int g = blockIdx.x % num_kv_heads;
-  const int s = blockIdx.x / num_kv_heads;
-  const int hq = num_kv_heads * kGroup;
-  const int head = g * kGroup + (threadIdx.x >> 6);
+    const int* __restrict__ ws_seg, int n_workers, int num_kv_heads) {
+  const int wid = blockIdx.x * kDecodeWaves + (threadIdx.x >> 6);
   const int d = threadIdx.x & 63;
-  int ctx = ctx_lens[s];
-  ctx = max(0, min(ctx, max_tokens));
-  const int np = (ctx + part_tokens - 1) / part_tokens;
-  float M = kNegInf;
-  for (int j = 0; j < np; ++j) M = fmaxf(M, ws_ml[((size_t)s * n_parts + j) * hq + head].x);
-  float L = 0.f, O = 0.f;
-  for (int j = 0; j < np; ++j) {
-    const size_t slot = ((size_t)s * n_parts + j) * hq + head;
-    const float2 ml = ws_ml[slot];
-    if (ml.x != kNegInf) {
-      const float f = fast_exp2(ml.x - M);
-      L += ml.y * f;
-      O += ws_o[slot * kHeadDim + d] * f;
+  if (wid >= n_workers) return;
+  const int* seg_first = ws_seg;
+  const int* seg_last = ws_seg + n_workers;
+  const int seg = seg_last[wid];
+  if (seg < 0 || wid + 1 >= n_workers || seg_first[wid + 1] != seg) return;
+  if (wid > 0 && seg_last[wid - 1] == seg) return;
+  int w1 = wid + 1;
+  while (w1 + 1 < n_workers && seg_first[w1 + 1] == seg) ++w1;
+  const int s = seg / num_kv_heads;
+  const int g = seg - s * num_kv_heads;
+  const int hq = num_kv_heads * kGroup;
+  for (int h = 0; h < kGroup; ++h) {
+    float M = kNegInf;
+    for (int v = wid; v <= w1; ++v) M = fmaxf(M, ws_ml[((size_t)seg + v) * kGroup + h].x);
+    float L = 0.f, O = 0.f;
+    if (M != kNegInf) {
+      for (int v = wid; v <= w1; ++v) {
+        const size_t slot = (size_t)seg + v;
+        const float2 ml = ws_ml[slot * kGroup + h];
+        if (ml.x != kNegInf) {
+          const float f = fast_exp2(ml.x - M);
+          L += ml.y * f;
+          O += ws_o[(slot * kGroup + h) * kHeadDim + d] * f;
+        } else {
+          O += ws_o[(slot * kGroup + h) * kHeadDim + d] * 0.f;  // carries a NaN marker
+        }
+      }
+    } else {
+      for (int v = wid; v <= w1; ++v)
+        O += ws_o[(((size_t)seg + v) * kGroup + h) * kHeadDim + d] * 0.f;
     }
+    out[((size_t)s * hq + g * kGroup + h) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : O);
   }
-  out[((size_t)s * hq + head) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : O * 0.f);
 }
 
 }  // namespace
 
-size_t decode_workspace_bytes(int n_seqs, int n_parts, int num_q_heads) {
-  if (n_parts <= 1) return 0;
-  const size_t slots = (size_t)n_seqs * n_parts * num_q_heads;
-  return slots * kHeadDim * sizeof(float) + slots * sizeof(float2);
+DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partition_tokens,
+                       int compute_units) {
+  DecodePlan p{};
+  const int64_t tiles_per_seq = std::max<int64_t>(1, ((int64_t)max_ctx_len + kTile - 1) / kTile);
+  const int64_t n_max = (int64_t)n_seqs * num_kv_heads * tiles_per_seq;
+  int64_t workers = partition_tokens > 0
+                        ? (n_max + partition_tokens / kTile - 1) / (partition_tokens / kTile)
+                        : (int64_t)kDecodeWaves * std::max(compute_units, 1);
+  const int64_t max_range = (int64_t)kDecodeMaxSeqsPerRange * num_kv_heads;
+  workers = std::max(workers, (n_max + max_range - 1) / max_range);
+  workers = std::max<int64_t>(1, std::min(workers, n_max));
+  p.n_max_tiles = n_max;
+  p.workers = workers;
+  p.tiles_per_worker = (n_max + workers - 1) / workers;
+  p.merge = workers > 1 && tiles_per_seq > 1;
+  if (p.merge) {
+    const int64_t slots = (int64_t)n_seqs * num_kv_heads + workers;
+    p.ws_bytes = (size_t)slots * kGroup * (kHeadDim * sizeof(float) + sizeof(float2)) +
+                 (size_t)2 * workers * sizeof(int);
+  }
+  return p;
 }
 
-hipError_t launch_decode(const LaunchGeom& geo, void* out, const void* q, const void* k_pool,
-                         const void* v_pool, const int32_t* block_tables, int max_blocks,
-                         const int32_t* ctx_lens, int n_seqs, int n_parts, int part_tokens,
+hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* out, const void* q,
+                         const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                         int max_blocks, const int32_t* ctx_lens, int n_seqs, int max_ctx_len,
                          float scale, void* workspace, hipStream_t stream) {
   const float qk_scale = scale * kLog2e;
   float* ws_o = nullptr;
   float2* ws_ml = nullptr;
-  if (n_parts > 1) {
-    const size_t slots = (size_t)n_seqs * n_parts * geo.num_q_heads;
+  int* ws_seg = nullptr;
+  if (plan.merge) {
+    const size_t slots = (size_t)n_seqs * geo.num_kv_heads + plan.workers;
     ws_o = static_cast<float*>(workspace);
-    ws_ml = reinterpret_cast<float2*>(ws_o + slots * kHeadDim);
+    ws_ml = reinterpret_cast<float2*>(ws_o + slots * kGroup * kHeadDim);
+    ws_seg = reinterpret_cast<int*>(ws_ml + slots * kGroup);
   }
-  const dim3 grid((unsigned)((size_t)n_seqs * geo.num_kv_heads * n_parts));
+  const int workers = (int)plan.workers;
+  const dim3 grid((unsigned)((workers + kDecodeWaves - 1) / kDecodeWaves));
   const dim3 block(256);
+  const int ctx_cap = std::min<int64_t>((int64_t)max_blocks * geo.block_size, max_ctx_len);
   auto* o = static_cast<uint16_t*>(out);
   auto* qq = static_cast<const uint16_t*>(q);
   auto* kp = static_cast<const uint16_t*>(k_pool);
   auto* vp = static_cast<const uint16_t*>(v_pool);
   if (geo.block_size == 16) {
-    hipLaunchKernelGGL(decode_part_kernel<16>, grid, block, 0, stream, o, ws_o, ws_ml, qq, kp, vp,
-                       block_tables, max_blocks, ctx_lens, geo.num_pages, geo.num_kv_heads,
-                       n_parts, part_tokens, qk_scale);
+    hipLaunchKernelGGL(decode_stream_kernel<16>, grid, block, 0, stream, o, ws_o, ws_ml, ws_seg,
+                       qq, kp, vp, block_tables, max_blocks, ctx_lens, n_seqs, ctx_cap,
+                       geo.num_pages, geo.num_kv_heads, workers, qk_scale);
   } else {
-    hipLaunchKernelGGL(decode_part_kernel<32>, grid, block, 0, stream, o, ws_o, ws_ml, qq, kp, vp,
-                       block_tables, max_blocks, ctx_lens, geo.num_pages, geo.num_kv_heads,
-                       n_parts, part_tokens, qk_scale);
+    hipLaunchKernelGGL(decode_stream_kernel<32>, grid, block, 0, stream, o, ws_o, ws_ml, ws_seg,
+                       qq, kp, vp, block_tables, max_blocks, ctx_lens, n_seqs, ctx_cap,
+                       geo.num_pages, geo.num_kv_heads, workers, qk_scale);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || n_parts == 1) return e;
-  const dim3 mgrid((unsigned)((size_t)n_seqs * geo.num_kv_heads));
-  const int max_tokens = (int)std::min<int64_t>((int64_t)max_blocks * geo.block_size,
-                                                  (int64_t)n_parts * part_tokens);
-  hipLaunchKernelGGL(decode_merge_kernel, mgrid, block, 0, stream, o, ws_o, ws_ml, ctx_lens,
-                     max_tokens, geo.num_kv_heads, n_parts, part_tokens);
+  if (e != hipSuccess || !plan.merge) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, grid, block, 0, stream, o, ws_o, ws_ml, ws_seg, workers,
+                     geo.num_kv_heads);
   return hipGetLastError();
 }
 

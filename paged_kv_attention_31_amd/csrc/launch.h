@@ -18,26 +18,35 @@ struct LaunchGeom {
   int num_kv_heads;
 };
 
-// Decode: tokens per KV partition are a multiple of this (one tile per wave, four waves).
-constexpr int kDecodeTile = 64;
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodePartQuantum = kDecodeTile * kDecodeWaves;  // 256
-
 hipError_t launch_kv_append(const LaunchGeom& geo, const void* k_new, const void* v_new,
                             void* k_pool, void* v_pool, const int32_t* block_tables,
                             int max_blocks, const int32_t* cu_new_lens, const int32_t* ctx_lens,
                             int n_seqs, int n_new_tokens, hipStream_t stream);
 
-// n_parts == 1: writes bf16 `out` directly and ignores the workspace.
-// n_parts  > 1: partition kernel writes fp32 partials to the workspace, merge kernel
-//               writes `out`.  Workspace: o [n_seqs][n_parts][Hq][64] fp32 followed by
-//               (m, l) [n_seqs][n_parts][Hq] float2.
-hipError_t launch_decode(const LaunchGeom& geo, void* out, const void* q, const void* k_pool,
-                         const void* v_pool, const int32_t* block_tables, int max_blocks,
-                         const int32_t* ctx_lens, int n_seqs, int n_parts, int part_tokens,
-                         float scale, void* workspace, hipStream_t stream);
+// Decode: workgroups of four waves; every wave is one stream-K worker.
+constexpr int kDecodeWaves = 4;
+// A worker's range is at most this many tiles per KV head (so it touches at most this
+// many sequences plus two, which its lanes can hold).
+constexpr int kDecodeMaxSeqsPerRange = 56;
 
-size_t decode_workspace_bytes(int n_seqs, int n_parts, int num_q_heads);
+// How a decode call is cut into workers; identical on the sizing and the launch side.
+struct DecodePlan {
+  int64_t n_max_tiles;       // upper bound of the tile stream: n_seqs * Hkv * ceil(max_ctx/64)
+  int64_t workers;           // worker waves
+  int64_t tiles_per_worker;  // ceil(n_max_tiles / workers)
+  bool merge;                // a segment may be cut between workers (partials + merge)
+  size_t ws_bytes;           // workspace needed (0 without merge)
+};
+
+// partition_tokens 0: 4 workers per compute unit; else enough workers that none streams
+// more than partition_tokens tokens (a multiple of 64).
+DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partition_tokens,
+                       int compute_units);
+
+hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* out, const void* q,
+                         const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                         int max_blocks, const int32_t* ctx_lens, int n_seqs, int max_ctx_len,
+                         float scale, void* workspace, hipStream_t stream);
 
 hipError_t launch_prefill(const LaunchGeom& geo, void* out, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* block_tables, int max_blocks,

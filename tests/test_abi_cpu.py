@@ -139,20 +139,45 @@ def test_decode_validation_returns_before_launch(lib):
     g = geom(num_pages=4096)
     assert _decode(lib, g=g, max_blocks=1024, max_ctx=16384, part=256) == _lib.PA_ERR_WORKSPACE
     need = lib.pa_decode_workspace_bytes(g, 2, 16384, 256)
-    assert need == 2 * 64 * 32 * (64 * 4 + 8)
+    assert need == _plan_ws(2, 16384, 8, 256)
     assert _decode(lib, g=g, max_blocks=1024, max_ctx=16384, part=256, ws=FAKE,
                    ws_bytes=need - 1) == _lib.PA_ERR_WORKSPACE
 
 
+def _plan_ws(n_seqs, max_ctx, hkv, part, cus=256):
+    """Workspace bytes of the documented decode plan (no device here: 256 compute units)."""
+    tiles = max(1, -(-max_ctx // 64))
+    n_max = n_seqs * hkv * tiles
+    workers = -(-n_max // (part // 64)) if part else 4 * cus
+    workers = max(workers, -(-n_max // (56 * hkv)))
+    workers = max(1, min(workers, n_max))
+    if workers == 1 or tiles == 1:
+        return 0
+    return (n_seqs * hkv + workers) * 4 * (64 * 4 + 8) + 2 * workers * 4
+
+
 def test_partition_choice(lib):
     g = geom(num_pages=20000, bs=32)
-    # explicit values are kept; automatic ones are multiples of 256 within the context
+    # explicit values bound the tokens one worker streams; they must be multiples of 64
     assert lib.pa_decode_partition_tokens(g, 16, 32768, 512) == 512
+    assert lib.pa_decode_partition_tokens(g, 16, 32768, 320) == 320
     assert lib.pa_decode_partition_tokens(g, 16, 32768, 100) == _lib.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_partition_tokens(g, 16, 32768, -64) == _lib.PA_ERR_INVALID_ARG
+    # automatic: 4 workers per compute unit, and never more than 56 tiles per KV head each
+    assert lib.pa_decode_partition_tokens(g, 16, 32768, 0) == 16 * 8 * 512 // 1024 * 64
+    assert lib.pa_decode_partition_tokens(g, 4096, 32768, 0) == 56 * 8 * 64
+    assert lib.pa_decode_partition_tokens(g, 4096, 32768, 1 << 20) == 56 * 8 * 64
     for n, ctx in ((16, 32768), (64, 2048), (128, 8192), (1, 37), (1, 1), (4096, 4096)):
         p = lib.pa_decode_partition_tokens(g, n, ctx, 0)
-        assert p > 0 and p % 256 == 0 and p <= max(256, ((ctx + 255) // 256) * 256)
-    assert lib.pa_decode_workspace_bytes(g, 1, 37, 0) == 0  # one partition: no workspace
+        assert p > 0 and p % 64 == 0
+    # the tile stream is counted in int32 on the device
+    assert lib.pa_decode_partition_tokens(g, 1 << 20, 1 << 20, 0) == _lib.PA_ERR_INVALID_ARG
+    # workspace: none when no segment can be cut (one tile per segment, or one worker)
+    assert lib.pa_decode_workspace_bytes(g, 1, 37, 0) == 0
+    assert lib.pa_decode_workspace_bytes(g, 64, 64, 0) == 0
+    for n, ctx, part in ((16, 32768, 0), (64, 2048, 0), (128, 8192, 0), (3, 300, 256),
+                         (1, 1000, 0), (21, 1025, 512)):
+        assert lib.pa_decode_workspace_bytes(g, n, ctx, part) == _plan_ws(n, ctx, 8, part)
 
 
 def test_prefill_and_append_validation(lib):

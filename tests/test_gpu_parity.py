@@ -20,6 +20,12 @@ from tests.helpers import oracle_decode, oracle_pools, oracle_prefill
 pytestmark = pytest.mark.gpu
 
 
+def torch_index(ids):
+    import torch
+
+    return torch.as_tensor(ids, dtype=torch.long, device="cuda:0")
+
+
 def _announce(msg):
     print(f"[gpu-test] {msg}", flush=True)
 
@@ -68,7 +74,7 @@ SWEEP_CTX = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 255, 256, 257, 300, 
 
 
 @pytest.mark.parametrize("bs", [16, 32])
-@pytest.mark.parametrize("part", [0, 256, 512])
+@pytest.mark.parametrize("part", [0, 64, 256, 512])
 def test_decode_length_sweep(bs, part):
     case = W.custom_case(SWEEP_CTX, [1] * len(SWEEP_CTX), block_size=bs, seed=50 + bs)
     _announce(f"decode sweep bs={bs} part={part}")
@@ -77,6 +83,61 @@ def test_decode_length_sweep(bs, part):
     kp, vp = oracle_pools(case)
     ref = oracle_decode(case, kp, vp)
     assert_close(out, ref, f"sweep bs={bs} part={part}")
+
+
+@pytest.mark.parametrize("part", [0, 128])
+def test_decode_many_sequences(part):
+    """700 sequences: the device-side prefix sum gives each of its 256 chunks three
+    sequences; workers start and end inside and across sequences."""
+    rng = np.random.default_rng(64)
+    ctx = rng.integers(1, 200, size=700, endpoint=True)
+    case = W.custom_case(ctx, [1] * 700, block_size=32, seed=64)
+    _announce(f"decode 700 sequences part={part}")
+    g = GpuCase(case)
+    out = g.decode(partition_tokens=part)
+    kp, vp = oracle_pools(case)
+    ref = oracle_decode(case, kp, vp)
+    assert_close(out, ref, f"700 sequences part={part}")
+
+
+def test_decode_beyond_16k_sequences_sampled():
+    """17000 sequences: each of the 256 prefix-sum chunks holds 67 sequences, so a worker
+    looking for its first sequence walks more than one block of 64.  Most contexts are
+    short (one tile); a few long ones are cut between workers."""
+    rng = np.random.default_rng(65)
+    n = 17000
+    ctx = rng.integers(4, 16, size=n, endpoint=True)
+    long_ids = [3, 66, 67, 130, 4000, 8191, 8192, 16999]
+    for i, s_ in enumerate(long_ids):
+        ctx[s_] = 150 + 97 * i
+    case = W.custom_case(ctx, [1] * n, block_size=16, seed=65)
+    _announce("decode 17000 sequences, sampled")
+    g = GpuCase(case)
+    out = g.decode(partition_tokens=64)
+    kp, vp = oracle_pools(case)
+    picks = sorted(set(long_ids + [0, 1, 2, 63, 64, 65, 68, 133, 134, 255, 256, 9000,
+                                   16934, 16998] + list(rng.integers(0, n, size=40))))
+    ref = oracle_decode(case, kp, vp, seqs=picks)
+    # the tolerance applies to the sampled rows together, as it does to a whole workload
+    # (a lone short context sits at the bf16 output-rounding floor of ~1e-3 mean-abs)
+    idx = torch_index(picks)
+    mx, mean = assert_close(out[idx], ref[picks], "17000 sequences (sampled rows)")
+    _announce(f"17000 sequences: max-abs {mx:.2e} mean-abs {mean:.2e}")
+    assert np.isfinite(out.float().cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("heads", [(4, 1), (8, 2), (64, 16)])
+@pytest.mark.parametrize("part", [0, 128])
+def test_decode_other_head_counts(heads, part):
+    hq, hkv = heads
+    case = W.custom_case([1, 70, 300, 1025, 64, 65], [1] * 6, block_size=16, seed=66 + hq,
+                         num_q_heads=hq, num_kv_heads=hkv)
+    _announce(f"decode heads {hq}/{hkv} part={part}")
+    g = GpuCase(case)
+    out = g.decode(partition_tokens=part)
+    kp, vp = oracle_pools(case)
+    ref = oracle_decode(case, kp, vp)
+    assert_close(out, ref, f"heads {hq}/{hkv} part={part}")
 
 
 def test_decode_empty_context_and_loose_max_ctx():
