@@ -251,18 +251,21 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   // scores, online-softmax update and P.V of the tile at cursor c, held in t
   auto compute = [&](const Tile& t, const Cursor& c, int slot) {
     const int nvalid = min(max(c.ctx - c.i * kTile, 0), kTile);
-    // q is re-read from LDS every tile as 16-byte broadcasts, one piece at a time; the
-    // opaque zero offset and the scheduling fences keep the compiler from hoisting all
-    // 32 reads (128 registers) out of the loop.
+    // q comes from LDS as 16-byte broadcasts, two pieces (4 heads each) in registers at a
+    // time: the reads of piece p + 2 are tied (through an empty asm) to the dot products
+    // of piece p, so the compiler can neither hoist all 32 reads (128 registers) nor
+    // leave a read waiting right before its use.
     int qofs = 0;
     asm volatile("" : "+s"(qofs));
-    const uint4* qrow = &q_sh[w][slot][0][0] + qofs;
     float x[kGroup] = {0.f, 0.f, 0.f, 0.f};
+    uint4 qa[kGroup], qb[kGroup];
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) qa[h] = q_sh[w][slot][h][qofs + 0];
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) qb[h] = q_sh[w][slot][h][qofs + 1];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      uint4 qc[kGroup];
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h) qc[h] = qrow[h * 8 + p];
+      uint4* qc = (p & 1) ? qb : qa;
 #pragma unroll
       for (int h = 0; h < kGroup; ++h) {
         float a = x[h];
@@ -272,23 +275,37 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
         a = dot2(t.k[p].w, qc[h].w, a);
         x[h] = a;
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (p + 2 < 8) {
+        asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+s"(qofs));
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h) qc[h] = q_sh[w][slot][h][qofs + p + 2];
+      }
     }
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) x[h] = lane < nvalid ? x[h] * qk_scale : kNegInf;
 
-    // p is rounded to bf16 once; the same rounded value feeds both the running sum and
-    // the P.V product, so the output is an exact convex combination of the V rows.
+    // Online-softmax update.  The tile maxima are wave-uniform, so the rescale of the
+    // running sums and outputs is one uniform branch, skipped when no head's maximum
+    // grew.  p is rounded to bf16 once; the same rounded value feeds both the running
+    // sum and the P.V product, so the output is an exact convex combination of V rows.
+    float mt[kGroup] = {x[0], x[1], x[2], x[3]};
+    wave_max4(mt[0], mt[1], mt[2], mt[3]);
+    if (mt[0] > m[0] || mt[1] > m[1] || mt[2] > m[2] || mt[3] > m[3]) {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        const float mn = fmaxf(m[h], mt[h]);
+        const float alpha = m[h] == mn ? 1.f : fast_exp2(m[h] - mn);  // 0 while m = -inf
+        l[h] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i][h] *= alpha;
+        m[h] = mn;
+      }
+    }
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
-      const float mn = fmaxf(m[h], wave_max(x[h]));
-      const float mref = mn == kNegInf ? 0.f : mn;  // a tile with no key keeps m = -inf
-      const float alpha = fast_exp2(m[h] - mref);   // 0 while m = -inf
+      const float mref = m[h] == kNegInf ? 0.f : m[h];  // a tile with no key keeps m = -inf
       const uint16_t pb = to_bf16(fast_exp2(x[h] - mref));  // 0 for tokens past the end
-      l[h] = l[h] * alpha + __uint_as_float((uint32_t)pb << 16);
-      m[h] = mn;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) acc[i][h] *= alpha;
+      l[h] += __uint_as_float((uint32_t)pb << 16);
       p_sh[w][h][lane] = pb;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -445,47 +462,94 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 
 // Combine the partials of every segment that range boundaries cut.  Wave wid owns the
 // segment its range ends in if that segment continues into range wid + 1 and did not
-// start in range wid - 1; it merges the partials of waves wid, wid + 1, ... (slots
-// seg + wave) in that order: M = max_j m_j, L = sum_j l_j 2^(m_j - M),
-// out = sum_j o_j 2^(m_j - M) / L.  Lane = head dimension.
+// start in range wid - 1; it merges the partials of waves wid .. w1 (slots seg + wave):
+// M = max_j m_j, L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L, with the
+// sums taken in ascending wave order.  Every step loads lane-parallel (worker lists,
+// then all (m, l) pairs, then the outputs) so an owner waits on a handful of memory
+// round trips, not one per partial.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
     const int* __restrict__ ws_seg, int n_workers, int num_kv_heads) {
   const int wid = blockIdx.x * kDecodeWaves + (threadIdx.x >> 6);
-  const int d = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   if (wid >= n_workers) return;
   const int* seg_first = ws_seg;
   const int* seg_last = ws_seg + n_workers;
-  const int seg = seg_last[wid];
-  if (seg < 0 || wid + 1 >= n_workers || seg_first[wid + 1] != seg) return;
-  if (wid > 0 && seg_last[wid - 1] == seg) return;
+  // lane 0: seg_last[wid], lane 1: seg_last[wid - 1], lane 2: seg_first[wid + 1]
+  int probe = -2;
+  if (lane == 0) probe = seg_last[wid];
+  if (lane == 1 && wid > 0) probe = seg_last[wid - 1];
+  if (lane == 2 && wid + 1 < n_workers) probe = seg_first[wid + 1];
+  const int seg = __builtin_amdgcn_readlane(probe, 0);
+  if (seg < 0) return;
+  if (__builtin_amdgcn_readlane(probe, 2) != seg) return;  // not cut at the range end
+  if (__builtin_amdgcn_readlane(probe, 1) == seg) return;  // started in an earlier range
+  // last wave covering the segment: waves wid+1 .. are checked 64 at a time
   int w1 = wid + 1;
-  while (w1 + 1 < n_workers && seg_first[w1 + 1] == seg) ++w1;
+  for (int base = wid + 2;; base += 64) {
+    const int v = base + lane;
+    const bool other = v >= n_workers || seg_first[v] != seg;
+    const uint64_t stop = __ballot(other);
+    if (stop) {
+      w1 = base + __ffsll((unsigned long long)stop) - 2;
+      break;
+    }
+  }
+  const int np = w1 - wid + 1;
   const int s = seg / num_kv_heads;
   const int g = seg - s * num_kv_heads;
   const int hq = num_kv_heads * kGroup;
+  const float2* ml = ws_ml + ((size_t)seg + wid) * kGroup;  // [np][4]
+  const float* o = ws_o + ((size_t)seg + wid) * kGroup * kHeadDim;  // [np][4][64]
+  float M[kGroup], L[kGroup], O[kGroup];
+#pragma unroll
   for (int h = 0; h < kGroup; ++h) {
-    float M = kNegInf;
-    for (int v = wid; v <= w1; ++v) M = fmaxf(M, ws_ml[((size_t)seg + v) * kGroup + h].x);
-    float L = 0.f, O = 0.f;
-    if (M != kNegInf) {
-      for (int v = wid; v <= w1; ++v) {
-        const size_t slot = (size_t)seg + v;
-        const float2 ml = ws_ml[slot * kGroup + h];
-        if (ml.x != kNegInf) {
-          const float f = fast_exp2(ml.x - M);
-          L += ml.y * f;
-          O += ws_o[(slot * kGroup + h) * kHeadDim + d] * f;
-        } else {
-          O += ws_o[(slot * kGroup + h) * kHeadDim + d] * 0.f;  // carries a NaN marker
+    M[h] = kNegInf;
+    L[h] = 0.f;
+    O[h] = 0.f;
+  }
+  // pass 1: maxima, 16 partials (64 (m, l) pairs) per load round
+  for (int b = 0; b < np; b += 16) {
+    const int j = b * kGroup + lane;
+    const float mj = j < np * kGroup ? ml[j].x : kNegInf;
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      float x = (lane & 3) == h ? mj : kNegInf;
+      x = wave_max(x);
+      M[h] = fmaxf(M[h], x);
+    }
+  }
+  // pass 2: weights and sums in ascending partial order
+  for (int v = 0; v < np; v += 4) {
+    float2 mlv[4][kGroup];
+    float ov[4][kGroup];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        const bool live = v + u < np;
+        mlv[u][h] = live ? ml[(v + u) * kGroup + h] : make_float2(kNegInf, 0.f);
+        ov[u][h] = live ? o[((size_t)(v + u) * kGroup + h) * kHeadDim + lane] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        if (v + u < np) {
+          const float f = M[h] == kNegInf || mlv[u][h].x == kNegInf
+                              ? 0.f
+                              : fast_exp2(mlv[u][h].x - M[h]);
+          L[h] += mlv[u][h].y * f;
+          O[h] += f == 0.f ? ov[u][h] * 0.f : ov[u][h] * f;  // a NaN marker survives
         }
       }
-    } else {
-      for (int v = wid; v <= w1; ++v)
-        O += ws_o[(((size_t)seg + v) * kGroup + h) * kHeadDim + d] * 0.f;
     }
-    out[((size_t)s * hq + g * kGroup + h) * kHeadDim + d] = to_bf16(L > 0.f ? O / L : O);
   }
+#pragma unroll
+  for (int h = 0; h < kGroup; ++h)
+    out[((size_t)s * hq + g * kGroup + h) * kHeadDim + lane] =
+        to_bf16(L[h] > 0.f ? O[h] / L[h] : O[h]);
 }
 
 }  // namespace
