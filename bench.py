@@ -50,6 +50,25 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def hbm_traffic(key: str):
+    """HBM bytes per launch that rocprofv3 FETCH_SIZE / WRITE_SIZE counters measured for this
+    workload's kernel (profiles/hbm_traffic.json, scaled by the 1 GiB copy calibration), or
+    None when there is no entry or the kernel source has changed since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            entry = json.load(f)["entries"][key]
+        with open(os.path.join(ROOT, entry["source"]), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    if digest != entry["source_sha256"]:
+        return None
+    return round(float(entry["bytes_per_launch"]))
+
+
 # ---------------------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, single thread, bounded sample
 # ---------------------------------------------------------------------------------------
@@ -315,9 +334,11 @@ def main() -> int:
     }
     if "decode_ms" in res:
         ach = res["decode_gbps"]
-        line["roofline"] = {"bound": "hbm", "kernel": "pa_decode (partition + merge)",
+        line["roofline"] = {"bound": "hbm",
+                            "kernel": "pa_decode (decode_stream_kernel + decode_merge_kernel)",
                             "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "frac": round(ach / HBM_PEAK_GBPS, 4),
+                            "traffic": hbm_traffic(args.workload),
                             "bytes_per_launch": res["decode_bytes_per_launch"],
                             "avg_launch_ms": round(res["decode_ms"], 5)}
     if "prefill_ms" in res:
@@ -325,7 +346,9 @@ def main() -> int:
         key = "roofline_prefill" if "roofline" in line else "roofline"
         line[key] = {"bound": "mfma", "kernel": "pa_prefill", "achieved": round(ach, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": hbm_traffic(args.workload + "-prefill" if key == "roofline_prefill"
+                                            else args.workload),
                      "flop_per_launch": res["prefill_flop_per_launch"],
                      "avg_launch_ms": round(res["prefill_ms"], 5)}
     line["append_ms_per_layer"] = round(res["append_ms"], 5)
