@@ -158,7 +158,8 @@ int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool
  *   max_ctx_len     host upper bound of ctx_lens (0 <= max_ctx_len <=
  *                   max_blocks_per_seq * block_size); with n_seqs it bounds the work
  *                   (n_seqs * num_kv_heads * ceil(max_ctx_len/64) < 2^31)
- *   scale           multiplies q.k before the softmax (1/sqrt(head_dim) = 0.125)
+ *   scale           multiplies q.k before the softmax: finite and > 0
+ *                   (1/sqrt(head_dim) = 0.125); anything else gives PA_ERR_INVALID_ARG
  *   partition_tokens  0: four workers per compute unit of the current device; else a
  *                   positive multiple of 64, and enough workers that none streams more
  *                   than that many tokens.  Either way no worker takes more than
@@ -196,6 +197,7 @@ int pa_decode(pa_geom_t g, void* out, const void* q, const void* k_pool, const v
  *   cu_q_lens   int32 [n_seqs+1] (device); q_len_s <= ctx_lens[s] required
  *   max_q_len   host upper bound of q_len_s (sizes the grid)
  *   max_ctx_len host upper bound of ctx_lens (<= max_blocks_per_seq * block_size)
+ *   scale       as for pa_decode: finite and > 0
  * ------------------------------------------------------------------------------- */
 int pa_prefill(pa_geom_t g, void* out, const void* q, const void* k_pool, const void* v_pool,
                const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -217,7 +217,7 @@ int pa_decode(pa_geom_t g, void* out, const void* q, const void* k_pool, const v
   if (st != PA_OK) return st;
   if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
   if ((int64_t)max_ctx_len > (int64_t)max_blocks_per_seq * g.block_size) return PA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PA_ERR_INVALID_ARG;
   if (n_seqs == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !ctx_lens) return PA_ERR_INVALID_ARG;
   const pa::DecodePlan plan = pa::plan_decode(n_seqs, max_ctx_len, g.num_kv_heads,
@@ -239,7 +239,7 @@ int pa_prefill(pa_geom_t g, void* out, const void* q, const void* k_pool, const 
     return PA_ERR_INVALID_ARG;
   if ((int64_t)max_ctx_len > (int64_t)max_blocks_per_seq * g.block_size) return PA_ERR_INVALID_ARG;
   if (max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PA_ERR_INVALID_ARG;
   if (n_seqs == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !ctx_lens)
     return PA_ERR_INVALID_ARG;

@@ -133,6 +133,8 @@ def test_decode_validation_returns_before_launch(lib):
     assert _decode(lib, max_ctx=65) == _lib.PA_ERR_INVALID_ARG  # > max_blocks * bs
     assert _decode(lib, part=100) == _lib.PA_ERR_INVALID_ARG
     assert _decode(lib, scale=float("nan")) == _lib.PA_ERR_INVALID_ARG
+    assert _decode(lib, scale=0.0) == _lib.PA_ERR_INVALID_ARG
+    assert _decode(lib, scale=-0.125) == _lib.PA_ERR_INVALID_ARG
     assert _decode(lib, n=-1) == _lib.PA_ERR_INVALID_ARG
     assert _decode(lib, n=0, out=None) == 0  # nothing to do
     # a split that needs a workspace, given none or too little
@@ -184,8 +186,12 @@ def test_prefill_and_append_validation(lib):
     g = geom()
     pf = lambda **k: lib.pa_prefill(k.get("g", g), k.get("out", FAKE), FAKE, FAKE, FAKE, FAKE,
                                     k.get("max_blocks", 4), FAKE, FAKE, k.get("n", 2),
-                                    k.get("max_q", 32), k.get("max_ctx", 64), 0.125, 1, None)
+                                    k.get("max_q", 32), k.get("max_ctx", 64),
+                                    k.get("scale", 0.125), 1, None)
     assert pf(out=None) == _lib.PA_ERR_INVALID_ARG
+    assert pf(scale=0.0) == _lib.PA_ERR_INVALID_ARG
+    assert pf(scale=-1.0) == _lib.PA_ERR_INVALID_ARG
+    assert pf(scale=float("inf")) == _lib.PA_ERR_INVALID_ARG
     assert pf(max_q=65, max_ctx=64) == _lib.PA_ERR_INVALID_ARG
     assert pf(max_ctx=65) == _lib.PA_ERR_INVALID_ARG
     assert pf(g=geom(hq=8)) == _lib.PA_ERR_UNSUPPORTED
