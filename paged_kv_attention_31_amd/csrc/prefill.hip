@@ -30,6 +30,8 @@
 // accumulator holds them, and the V^T operand is read in that same key order).
 // scale * log2(e) is folded into one FMA ahead of exp2; the output is rescaled only when
 // some row's running maximum grew.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -40,6 +42,7 @@ namespace {
 constexpr int kQTile = 32;   // query positions per workgroup
 constexpr int kStage = 64;   // keys per LDS stage
 constexpr int kThreads = 256;
+constexpr float kLazy = 8.f;  // log2 of the largest p the lazy rescale lets through
 
 // Own value and the value of lane j ^ 32 (the two half-waves hold the same query's
 // keys), in either order, from one v_permlane32_swap (it exchanges the upper half of its
@@ -50,7 +53,7 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ void pair_swap(float x, float& a, float& b) {
   unsigned u = __builtin_bit_cast(unsigned, x);
   unsigned v = u;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(u), "+v"(v));
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(u), "+v"(v));  // pure: schedulable
   a = __builtin_bit_cast(float, u);
   b = __builtin_bit_cast(float, v);
 }
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int pos_first = ctx - qlen + tile * kQTile;          // smallest in the tile
   const int pos_last = ctx - qlen + min(tile * kQTile + kQTile - 1, qlen - 1);
   const int kend = causal ? min(ctx, pos_last + 1) : ctx;    // keys [0, kend)
+  const int klim = causal ? min(ctx, qpos + 1) : ctx;        // this lane's row sees keys < klim
   const int n_stages = (kend + kStage - 1) / kStage;
   const int last_blk = kend > 0 ? (kend - 1) / BS : 0;
 
@@ -130,88 +134,110 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
   // ---- staging: thread t moves K chunks t, t+256 and V chunks t, t+256 of a stage ------
   // chunk c of a stage: page c / KCH, 16-byte piece c % KCH of that page's head slice.
-  bool bad = false;
-  uint4 kr0, kr1, vr0, vr1;  // the thread's two K and two V chunks of the next stage
-  auto chunk_base = [&](int k0, int c) -> size_t {
-    const int pj = c / KCH;
-    int pid = bt[min(k0 / BS + pj, last_blk)];
-    if ((unsigned)pid >= (unsigned)num_pages) { bad = true; pid = 0; }
-    return (size_t)pid * page_stride + (size_t)(c - pj * KCH) * 8;
+  // A thread's share of a stage: K and V chunks tid and tid + 256 (16 bytes each).
+  struct StageRegs {  // plain vector types: HIP's uint4 copies go through the stack
+    u32x4_t k0, k1, v0, v1;
   };
-  auto stage_load = [&](int st) {
-    const int k0 = st * kStage;
-    const size_t b0 = chunk_base(k0, tid);
-    const size_t b1 = chunk_base(k0, tid + kThreads);
-    kr0 = *reinterpret_cast<const uint4*>(k_head + b0);
-    vr0 = *reinterpret_cast<const uint4*>(v_head + b0);
-    kr1 = *reinterpret_cast<const uint4*>(k_head + b1);
-    vr1 = *reinterpret_cast<const uint4*>(v_head + b1);
+  // Block-table entries of the pages holding the thread's two chunks of stage st, pages
+  // past the last needed block repeating it.
+  auto stage_pids = [&](int st, int& pa, int& pb) __attribute__((always_inline)) {
+    const int blk0 = st * (kStage / BS);
+    pa = bt[min(blk0 + tid / KCH, last_blk)];
+    pb = bt[min(blk0 + (tid + kThreads) / KCH, last_blk)];
+  };
+  // Issue the thread's loads of a stage.  `live` false (a stage past the end) points every
+  // lane at one 16-byte piece, so each load instruction fetches one line.
+  bool bad = false;
+  auto stage_load = [&](StageRegs& r, int pa, int pb, bool live) __attribute__((always_inline)) {
+    if ((unsigned)pa >= (unsigned)num_pages) { bad = true; pa = 0; }
+    if ((unsigned)pb >= (unsigned)num_pages) { bad = true; pb = 0; }
+    const size_t ba = (size_t)pa * page_stride + (live ? (size_t)(tid % KCH) * 8 : 0);
+    const size_t bb = (size_t)pb * page_stride + (live ? (size_t)((tid + kThreads) % KCH) * 8 : 0);
+    r.k0 = *reinterpret_cast<const u32x4_t*>(k_head + ba);
+    r.v0 = *reinterpret_cast<const u32x4_t*>(v_head + ba);
+    r.k1 = *reinterpret_cast<const u32x4_t*>(k_head + bb);
+    r.v1 = *reinterpret_cast<const u32x4_t*>(v_head + bb);
   };
   // V chunk c: dim row within / (BS/8), keys 8 * (within % (BS/8)) .. +8 of page c / KCH;
   // keys at or past the context end are cleared
-  auto store_v = [&](int k0, int c, uint4 vv, int buf) {
+  auto store_v = [&](int k0, int c, u32x4_t vv, int buf) __attribute__((always_inline)) {
     const int pj = c / KCH;
     const int within = c - pj * KCH;
     const int row = within / (BS / 8);
     const int c8 = within - row * (BS / 8);
     const int key0 = k0 + pj * BS + c8 * 8;
     if (key0 + 8 > ctx) {
-      uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (key0 + e >= ctx) wv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        if (key0 + e >= ctx) vv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
       }
-      vv = make_uint4(wv[0], wv[1], wv[2], wv[3]);
     }
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
     uint16_t* dst = &sh.v[buf][pj][row][c8 * 8];
-    *reinterpret_cast<uint2*>(dst) = make_uint2(vv.x, vv.y);
-    *reinterpret_cast<uint2*>(dst + 4) = make_uint2(vv.z, vv.w);
+    *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{vv[0], vv[1]};
+    *reinterpret_cast<u32x2_t*>(dst + 4) = u32x2_t{vv[2], vv[3]};
   };
-  auto stage_store = [&](int st, int buf) {
+  auto stage_store = [&](const StageRegs& r, int st, int buf) __attribute__((always_inline)) {
     const int k0 = st * kStage;
-    *reinterpret_cast<uint4*>(&sh.k[buf][tid * 8]) = kr0;
-    *reinterpret_cast<uint4*>(&sh.k[buf][(tid + kThreads) * 8]) = kr1;
-    store_v(k0, tid, vr0, buf);
-    store_v(k0, tid + kThreads, vr1, buf);
+    *reinterpret_cast<u32x4_t*>(&sh.k[buf][tid * 8]) = r.k0;
+    *reinterpret_cast<u32x4_t*>(&sh.k[buf][(tid + kThreads) * 8]) = r.k1;
+    store_v(k0, tid, r.v0, buf);
+    store_v(k0, tid + kThreads, r.v1, buf);
   };
 
   float m = kNegInf, lsum = 0.f;  // this lane's query row: running max (scaled) and sum
   f32x16_t o0 = {}, o1 = {};
 
-  // one 32-key half of a stage: keys k0 + 32 * hh .. +32
-  auto compute_half = [&](int buf, int k0, int hh) {
-    const int kb = k0 + 32 * hh;
-    // ---- S^T = K . Q^T ------------------------------------------------------------------
+  // A stage is two 32-key halves.  Per half: S^T = K . Q^T (4 MFMAs), the online-softmax
+  // update (VALU), O^T += V^T . P^T (4 MFMAs).  The stage issues both halves' S^T products
+  // first, so the softmax of one half runs on the VALU while the matrix core works on the
+  // other's products; reductions are trees rather than chains.
+  // K operands of one half (4 x 16 bytes: pieces 2 st + half of the lane's key row)
+  struct KOps {
+    u32x4_t a[4];
+  };
+  auto read_k = [&](int buf, int hh, KOps& ko) __attribute__((always_inline)) {
     const int kk = 32 * hh + j;  // key within the stage held as A row by this lane
     const uint16_t* krow =
         &sh.k[buf][(kk / BS) * (KCH * 8) + (kk % BS) * 8 + half * BS * 8];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) ko.a[st] = *reinterpret_cast<const u32x4_t*>(krow + st * 2 * BS * 8);
+  };
+  auto qk = [&](const KOps& ko) __attribute__((always_inline)) -> f32x16_t {
     f32x16_t sacc = {};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const uint4 a = *reinterpret_cast<const uint4*>(krow + st * 2 * BS * 8);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[st],
-                                                     sacc, 0, 0, 0);
-    }
-    // ---- mask, online softmax -----------------------------------------------------------
+    for (int st = 0; st < 4; ++st)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ko.a[st]),
+                                                     qb[st], sacc, 0, 0, 0);
+    return sacc;
+  };
+  // mask, online-softmax update; returns p (bf16 pairs) in the S^T accumulator order
+  auto softmax = [&](const f32x16_t& sacc, int kb, uint32_t (&pk)[8])
+      __attribute__((always_inline)) {
     float sv[16];
-    const bool need_mask = (kb + 32 > ctx) || (causal && kb + 31 > pos_first);
+    if ((kb + 32 > ctx) || (causal && kb + 31 > pos_first)) {  // the half crosses a limit
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = sacc[r];
-      if (need_mask) {
+      for (int r = 0; r < 16; ++r) {
         const int kr = kb + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (kr >= ctx || (causal && kr > qpos)) x = kNegInf;
+        sv[r] = kr < klim ? sacc[r] : kNegInf;
       }
-      sv[r] = x;
-    }
-    float mt = sv[0];
+    } else {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sv[r]);
-    mt = pair_max(mt) * qk_scale;        // scores are scaled by qk_scale > 0 below
-    const float mn = fmaxf(m, mt);
-    const float mref = (mn == kNegInf) ? 0.f : mn;
-    if (__ballot(mn != m)) {  // some row's maximum grew: rescale sums and outputs
-      const float alpha = fast_exp2(m - mref);  // 0 while m = -inf
+      for (int r = 0; r < 16; ++r) sv[r] = sacc[r];
+    }
+    float t4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      t4[r] = fmaxf(fmaxf(sv[4 * r], sv[4 * r + 1]), fmaxf(sv[4 * r + 2], sv[4 * r + 3]));
+    float mt = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+    mt = pair_max(mt) * qk_scale;  // scores are scaled by qk_scale > 0 below
+    // Lazy rescale: the running maximum m is only a reference point, any value works as
+    // long as sums and outputs use the same one.  It is moved (and sums and outputs
+    // rescaled) only when a row's new maximum exceeds it by more than 2^kLazy, so p stays
+    // <= 2^kLazy and the rescale runs about once per row instead of nearly every tile.
+    if (__ballot(mt > m + kLazy)) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = m == kNegInf ? 0.f : fast_exp2(m - mn);
       lsum *= alpha;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -220,61 +246,123 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
       m = mn;
     }
+    const float mref = (m == kNegInf) ? 0.f : m;
     // p = 2^(s * qk_scale - m), rounded to bf16 once: the P.V operand; the running sum
     // adds those same rounded values (a dot with (1, 1)), so the normaliser matches.
-    uint32_t pk[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       pk[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(sv[2 * i], qk_scale, -mref)),
                           fast_exp2(__builtin_fmaf(sv[2 * i + 1], qk_scale, -mref)));
-    float ps = 0.f;
+    float pa = 0.f, pb = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ps = dot2(pk[i], 0x3F803F80u, ps);
-    lsum += ps;
-
-    // ---- O^T += V^T . P^T ---------------------------------------------------------------
-    // Element e (0..7) of lane half h's B operand for k-step ks is the score of key
-    // 16 ks + (e < 4 ? 0 : 8) + 4 h + (e & 3) (the S^T accumulator order), so the V^T
-    // operand reads the two 4-key runs at 16 ks + 4 h and 16 ks + 8 + 4 h.
+    for (int i = 0; i < 8; i += 2) {
+      pa = dot2(pk[i], 0x3F803F80u, pa);
+      pb = dot2(pk[i + 1], 0x3F803F80u, pb);
+    }
+    lsum += pa + pb;
+  };
+  // O^T += V^T . P^T.  Element e (0..7) of lane half h's B operand for k-step ks is the
+  // score of key 16 ks + (e < 4 ? 0 : 8) + 4 h + (e & 3) (the S^T accumulator order), so
+  // the V^T operand reads the two 4-key runs at 16 ks + 4 h and 16 ks + 8 + 4 h.
+  struct VOps {
+    u32x4_t a[2][2];  // [ks][mb]
+  };
+  auto read_v = [&](int buf, int hh, VOps& vo) __attribute__((always_inline)) {
+    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const uint4 pb = make_uint4(pk[4 * ks + 0], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]);
       const int kr0 = 32 * hh + 16 * ks + 4 * half;  // first key (within the stage) of run 0
       const int pj = kr0 / BS;
       const int slot = kr0 % BS;  // runs at slot and slot + 8 stay inside one page
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const uint16_t* vr = &sh.v[buf][pj][32 * mb + j][slot];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-        const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        if (mb == 0)
-          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, pb), o0, 0,
-                                                       0, 0);
-        else
-          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, pb), o1, 0,
-                                                       0, 0);
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 8);
+        vo.a[ks][mb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
       }
     }
   };
+  auto pv = [&](const VOps& vo, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t pb = {pk[4 * ks + 0], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vo.a[ks][0]),
+                                                   __builtin_bit_cast(bf16x8_t, pb), o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vo.a[ks][1]),
+                                                   __builtin_bit_cast(bf16x8_t, pb), o1, 0, 0, 0);
+    }
+  };
+  // Both halves run even when the second lies past kend: it is then fully masked
+  // (p = 0, no rescale) and adds nothing, and the straight-line order keeps the second
+  // half's S^T products in flight during the first half's softmax.
+  // The LDS operand reads of the whole stage go out first (they depend on nothing the
+  // stage computes), so the wave waits on LDS once per stage rather than once per MFMA.
+  auto compute_stage = [&](int buf, int k0) __attribute__((always_inline)) {
+    KOps k0o, k1o;
+    VOps v0o, v1o;
+    read_k(buf, 0, k0o);
+    read_k(buf, 1, k1o);
+    read_v(buf, 0, v0o);
+    read_v(buf, 1, v1o);
+    uint32_t p0[8], p1[8];
+    const f32x16_t s0 = qk(k0o);
+    const f32x16_t s1 = qk(k1o);
+    softmax(s0, k0, p0);
+    pv(v0o, p0);
+    softmax(s1, k0 + 32, p1);
+    pv(v1o, p1);
+  };
 
+  // Stage pipeline.  At iteration st: LDS buffer st % 2 holds stage st, the registers of
+  // stage st + 1 are in flight (issued an iteration ago), and the block-table entries of
+  // stage st + 2 have arrived.  The iteration issues the block-table loads of stage st + 3
+  // and the K/V loads of stage st + 2, computes stage st from LDS, stores stage st + 1
+  // to the other buffer and meets the barrier.  Every load is issued unconditionally
+  // (stages past the end are the cheap `live = false` kind) and the loop is unrolled by
+  // two with fixed registers per parity, so the compiler's wait counts let the loads of
+  // stage st + 2 stay in flight across the store of stage st + 1.
   if (tid == 0) bad_sh = 0;
+  StageRegs ra, rb;   // stage u lives in ra for even u, rb for odd u
+  int pa_e, pb_e, pa_o, pb_o;  // block-table entries for even / odd stages
   if (n_stages > 0) {
-    stage_load(0);
-    stage_store(0, 0);
+    int p0a, p0b;
+    stage_pids(0, p0a, p0b);
+    stage_pids(1, pa_o, pb_o);
+    stage_load(ra, p0a, p0b, true);
+    stage_pids(2, pa_e, pb_e);
+    stage_load(rb, pa_o, pb_o, 1 < n_stages);
+    stage_store(ra, 0, 0);
   }
   __syncthreads();
-  for (int st = 0; st < n_stages; ++st) {
+  // One iteration for stage st of parity P (0: st even).  Registers are chosen by name at
+  // compile time (stage u lives in ra for even u, rb for odd u; the block-table entries of
+  // stage u in pa_e/pb_e or pa_o/pb_o by the parity of u) so nothing is addressed through
+  // a pointer and no register set spills to scratch.
+  auto iteration = [&](int st, auto parity) __attribute__((always_inline)) {
+    constexpr int P = decltype(parity)::value;
     const int buf = st & 1;
-    const bool more = st + 1 < n_stages;
-    if (more) stage_load(st + 1);
-    const int k0 = st * kStage;
-    compute_half(buf, k0, 0);
-    if (k0 + 32 < kend) compute_half(buf, k0, 1);
-    if (more) stage_store(st + 1, buf ^ 1);
+    // block-table entries of stage st + 3 (parity !P) ; K/V of stage st + 2 (parity P)
+    if constexpr (P == 0) {
+      stage_pids(st + 3, pa_o, pb_o);
+      stage_load(ra, pa_e, pb_e, st + 2 < n_stages);
+    } else {
+      stage_pids(st + 3, pa_e, pb_e);
+      stage_load(rb, pa_o, pb_o, st + 2 < n_stages);
+    }
+    compute_stage(buf, st * kStage);
+    if (st + 1 < n_stages) {
+      if constexpr (P == 0)
+        stage_store(rb, st + 1, buf ^ 1);
+      else
+        stage_store(ra, st + 1, buf ^ 1);
+    }
     __syncthreads();
+  };
+  for (int st = 0; st < n_stages; st += 2) {
+    iteration(st, std::integral_constant<int, 0>{});
+    if (st + 1 >= n_stages) break;
+    iteration(st + 1, std::integral_constant<int, 1>{});
   }
   if (bad) bad_sh = 1;
   __syncthreads();
