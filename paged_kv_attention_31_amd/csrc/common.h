@@ -16,6 +16,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // 16 bytes, register-friendly
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // ---- bf16 bit patterns -----------------------------------------------------------------
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }

@@ -57,10 +57,14 @@ __device__ __forceinline__ void pair_swap(float x, float& a, float& b) {
   a = __builtin_bit_cast(float, u);
   b = __builtin_bit_cast(float, v);
 }
+// IEEE maximum (NaN-propagating): lowers to v_maximum3_f32 without the operand
+// canonicalisation that fmaxf needs on MFMA results
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 __device__ __forceinline__ float pair_max(float x) {
   float a, b;
   pair_swap(x, a, b);
-  return fmaxf(a, b);
+  return vmax(a, b);
 }
 __device__ __forceinline__ float pair_sum(float x) {
   float a, b;
@@ -77,7 +81,7 @@ struct PrefillLds {
 };
 
 template <int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks,
@@ -88,12 +92,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int VROW = Lds::VROW;
   constexpr int KCH = 8 * BS;  // 16-byte chunks of one page's K (or V) head slice
   __shared__ __attribute__((aligned(16))) Lds sh;
-  __shared__ int bad_sh;
 
+  // Work order: tiles longest first (highest query positions see the most keys), the
+  // sequences of one tile level rotated by the level.  The hardware hands workgroups to
+  // the XCDs (bid mod 8) and, inside one, to its shader engines in turn; without the
+  // rotation a sequence would land on the same engine at every level and the engines'
+  // loads would differ by the sequences' lengths.
   const int bid = blockIdx.x;
   const int g = bid % num_kv_heads;
-  const int s = (bid / num_kv_heads) % n_seqs;
-  const int tile = n_qtiles - 1 - bid / (num_kv_heads * n_seqs);
+  const int level = bid / (num_kv_heads * n_seqs);
+  const int s = ((bid / num_kv_heads) % n_seqs + level) % n_seqs;
+  const int tile = n_qtiles - 1 - level;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -137,6 +146,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // A thread's share of a stage: K and V chunks tid and tid + 256 (16 bytes each).
   struct StageRegs {  // plain vector types: HIP's uint4 copies go through the stack
     u32x4_t k0, k1, v0, v1;
+    int bad;  // bit 0 / 1: the page of chunk t / t + 256 was out of range
   };
   // Block-table entries of the pages holding the thread's two chunks of stage st, pages
   // past the last needed block repeating it.
@@ -146,11 +156,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     pb = bt[min(blk0 + (tid + kThreads) / KCH, last_blk)];
   };
   // Issue the thread's loads of a stage.  `live` false (a stage past the end) points every
-  // lane at one 16-byte piece, so each load instruction fetches one line.
-  bool bad = false;
+  // lane at one 16-byte piece, so each load instruction fetches one line.  A page id out
+  // of range reads page 0 instead and marks the chunk, which is staged as K = NaN, V = 0.
   auto stage_load = [&](StageRegs& r, int pa, int pb, bool live) __attribute__((always_inline)) {
-    if ((unsigned)pa >= (unsigned)num_pages) { bad = true; pa = 0; }
-    if ((unsigned)pb >= (unsigned)num_pages) { bad = true; pb = 0; }
+    r.bad = 0;
+    if ((unsigned)pa >= (unsigned)num_pages) { r.bad |= 1; pa = 0; }
+    if ((unsigned)pb >= (unsigned)num_pages) { r.bad |= 2; pb = 0; }
     const size_t ba = (size_t)pa * page_stride + (live ? (size_t)(tid % KCH) * 8 : 0);
     const size_t bb = (size_t)pb * page_stride + (live ? (size_t)((tid + kThreads) % KCH) * 8 : 0);
     r.k0 = *reinterpret_cast<const u32x4_t*>(k_head + ba);
@@ -160,32 +171,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
   // V chunk c: dim row within / (BS/8), keys 8 * (within % (BS/8)) .. +8 of page c / KCH;
   // keys at or past the context end are cleared
-  auto store_v = [&](int k0, int c, u32x4_t vv, int buf) __attribute__((always_inline)) {
+  auto store_v = [&](int k0, bool tail, int c, u32x4_t vv, int buf) __attribute__((always_inline)) {
     const int pj = c / KCH;
     const int within = c - pj * KCH;
     const int row = within / (BS / 8);
     const int c8 = within - row * (BS / 8);
     const int key0 = k0 + pj * BS + c8 * 8;
-    if (key0 + 8 > ctx) {
+    if (tail && key0 + 8 > ctx) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (key0 + e >= ctx) vv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
       }
     }
-    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
     uint16_t* dst = &sh.v[buf][pj][row][c8 * 8];
     *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{vv[0], vv[1]};
     *reinterpret_cast<u32x2_t*>(dst + 4) = u32x2_t{vv[2], vv[3]};
   };
-  auto stage_store = [&](const StageRegs& r, int st, int buf) __attribute__((always_inline)) {
+  // Rows that see a key of an out-of-range page get NaN scores (and so a NaN output);
+  // V = 0 keeps the page's stale values out of the rows that mask those keys.
+  auto stage_store = [&](StageRegs& r, int st, int buf) __attribute__((always_inline)) {
+    if (__builtin_expect(__ballot(r.bad != 0) != 0, 0)) {
+      const u32x4_t nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+      const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+      if (r.bad & 1) { r.k0 = nan4; r.v0 = zero4; }
+      if (r.bad & 2) { r.k1 = nan4; r.v1 = zero4; }
+    }
     const int k0 = st * kStage;
+    const bool tail = k0 + kStage > ctx;  // the stage reaches past the context end
     *reinterpret_cast<u32x4_t*>(&sh.k[buf][tid * 8]) = r.k0;
     *reinterpret_cast<u32x4_t*>(&sh.k[buf][(tid + kThreads) * 8]) = r.k1;
-    store_v(k0, tid, r.v0, buf);
-    store_v(k0, tid + kThreads, r.v1, buf);
+    store_v(k0, tail, tid, r.v0, buf);
+    store_v(k0, tail, tid + kThreads, r.v1, buf);
   };
 
-  float m = kNegInf, lsum = 0.f;  // this lane's query row: running max (scaled) and sum
+  // This lane's query row: reference maximum m (scaled), m + kLazy, the FMA addend -m (0
+  // while m is -inf, so masked scores give 2^-inf = 0), and the running sum.
+  float m = kNegInf, mthr = kNegInf, negm = 0.f, lsum = 0.f;
+  const int lim_lane = klim - 4 * half;  // key offsets from a half's base below this are visible
   f32x16_t o0 = {}, o1 = {};
 
   // A stage is two 32-key halves.  Per half: S^T = K . Q^T (4 MFMAs), the online-softmax
@@ -216,27 +238,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       __attribute__((always_inline)) {
     float sv[16];
     if ((kb + 32 > ctx) || (causal && kb + 31 > pos_first)) {  // the half crosses a limit
+      // element r is key kb + 8 (r / 4) + 4 half + r % 4, visible while below klim
+      const int lim = lim_lane - kb;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = kb + 8 * (r >> 2) + 4 * half + (r & 3);
-        sv[r] = kr < klim ? sacc[r] : kNegInf;
-      }
+      for (int r = 0; r < 16; ++r) sv[r] = (8 * (r >> 2) + (r & 3)) < lim ? sacc[r] : kNegInf;
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = sacc[r];
     }
-    float t4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      t4[r] = fmaxf(fmaxf(sv[4 * r], sv[4 * r + 1]), fmaxf(sv[4 * r + 2], sv[4 * r + 3]));
-    float mt = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
+    const float t0 = vmax3(sv[0], sv[1], sv[2]), t1 = vmax3(sv[3], sv[4], sv[5]);
+    const float t2 = vmax3(sv[6], sv[7], sv[8]), t3 = vmax3(sv[9], sv[10], sv[11]);
+    const float t4 = vmax3(sv[12], sv[13], sv[14]);
+    float mt = vmax3(vmax3(t0, t1, t2), vmax(t3, t4), sv[15]);
     mt = pair_max(mt) * qk_scale;  // scores are scaled by qk_scale > 0 below
     // Lazy rescale: the running maximum m is only a reference point, any value works as
     // long as sums and outputs use the same one.  It is moved (and sums and outputs
     // rescaled) only when a row's new maximum exceeds it by more than 2^kLazy, so p stays
     // <= 2^kLazy and the rescale runs about once per row instead of nearly every tile.
-    if (__ballot(mt > m + kLazy)) {
-      const float mn = fmaxf(m, mt);
+    if (__ballot(mt > mthr)) {
+      const float mn = vmax(m, mt);
       const float alpha = m == kNegInf ? 0.f : fast_exp2(m - mn);
       lsum *= alpha;
 #pragma unroll
@@ -245,14 +265,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         o1[r] *= alpha;
       }
       m = mn;
+      mthr = m + kLazy;
+      negm = m == kNegInf ? 0.f : -m;
     }
-    const float mref = (m == kNegInf) ? 0.f : m;
     // p = 2^(s * qk_scale - m), rounded to bf16 once: the P.V operand; the running sum
     // adds those same rounded values (a dot with (1, 1)), so the normaliser matches.
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      pk[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(sv[2 * i], qk_scale, -mref)),
-                          fast_exp2(__builtin_fmaf(sv[2 * i + 1], qk_scale, -mref)));
+      pk[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(sv[2 * i], qk_scale, negm)),
+                          fast_exp2(__builtin_fmaf(sv[2 * i + 1], qk_scale, negm)));
     float pa = 0.f, pb = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
@@ -268,7 +289,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     u32x4_t a[2][2];  // [ks][mb]
   };
   auto read_v = [&](int buf, int hh, VOps& vo) __attribute__((always_inline)) {
-    typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int kr0 = 32 * hh + 16 * ks + 4 * half;  // first key (within the stage) of run 0
@@ -295,23 +315,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
   // Both halves run even when the second lies past kend: it is then fully masked
   // (p = 0, no rescale) and adds nothing, and the straight-line order keeps the second
-  // half's S^T products in flight during the first half's softmax.
-  // The LDS operand reads of the whole stage go out first (they depend on nothing the
-  // stage computes), so the wave waits on LDS once per stage rather than once per MFMA.
+  // half's S^T products in flight during the first half's softmax.  The K operands of
+  // the stage are read from LDS up front; each half's V operands just before its
+  // softmax (holding all of them would cost the third wave per SIMD its registers).
   auto compute_stage = [&](int buf, int k0) __attribute__((always_inline)) {
     KOps k0o, k1o;
-    VOps v0o, v1o;
     read_k(buf, 0, k0o);
     read_k(buf, 1, k1o);
-    read_v(buf, 0, v0o);
-    read_v(buf, 1, v1o);
     uint32_t p0[8], p1[8];
     const f32x16_t s0 = qk(k0o);
     const f32x16_t s1 = qk(k1o);
-    softmax(s0, k0, p0);
-    pv(v0o, p0);
-    softmax(s1, k0 + 32, p1);
-    pv(v1o, p1);
+    {
+      VOps v0o;
+      read_v(buf, 0, v0o);
+      softmax(s0, k0, p0);
+      pv(v0o, p0);
+    }
+    {
+      VOps v1o;
+      read_v(buf, 1, v1o);
+      softmax(s1, k0 + 32, p1);
+      pv(v1o, p1);
+    }
   };
 
   // Stage pipeline.  At iteration st: LDS buffer st % 2 holds stage st, the registers of
@@ -322,7 +347,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // (stages past the end are the cheap `live = false` kind) and the loop is unrolled by
   // two with fixed registers per parity, so the compiler's wait counts let the loads of
   // stage st + 2 stay in flight across the store of stage st + 1.
-  if (tid == 0) bad_sh = 0;
   StageRegs ra, rb;   // stage u lives in ra for even u, rb for odd u
   int pa_e, pb_e, pa_o, pb_o;  // block-table entries for even / odd stages
   if (n_stages > 0) {
@@ -364,13 +388,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     if (st + 1 >= n_stages) break;
     iteration(st + 1, std::integral_constant<int, 1>{});
   }
-  if (bad) bad_sh = 1;
-  __syncthreads();
 
   // ---- normalise and store: lane holds dims 8*(r/4) + 4*half + (r%4) of query j ----------
   const float ltot = pair_sum(lsum);
-  float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (bad_sh) inv = __builtin_nanf("");
+  const float inv = ltot == 0.f ? 0.f : 1.f / ltot;  // a NaN sum stays NaN
   if (!qvalid) return;
   uint16_t* op = out + ((size_t)(qa + qi) * hq + head) * kHeadDim + 4 * half;
 #pragma unroll

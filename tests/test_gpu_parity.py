@@ -256,6 +256,28 @@ def test_prefill_chunked_ragged(bs, causal):
     assert_close(out, ref, f"prefill bs={bs} causal={causal}")
 
 
+def test_prefill_out_of_range_page_gives_nan_rows():
+    # a block-table entry outside the pool: exactly the rows whose keys reach that block
+    # come out NaN (every head), the others match the oracle
+    case = W.custom_case([200, 90], [200, 90], kind="prefill", block_size=16, seed=91)
+    kp, vp = oracle_pools(case)
+    ref = oracle_prefill(case, kp, vp)
+    g = GpuCase(case)
+    bt = case.block_tables.copy()
+    blk = 5  # keys 80 .. 95 of sequence 0
+    bt[0, blk] = case.num_pages + 3
+    from tests.gpu_helpers import i32_dev
+    g.pre_bt = i32_dev(bt)
+    out_t = g.prefill()
+    out = out_t.float().cpu().numpy()
+    pos = np.arange(200)  # sequence 0 is a whole prompt: row i sits at position i
+    sees = pos >= blk * 16
+    assert np.isnan(out[:200][sees]).all()
+    assert not np.isnan(out[:200][~sees]).any() and not np.isnan(out[200:]).any()
+    ok = np.nonzero(np.concatenate([~sees, np.ones(90, bool)]))[0]
+    assert_close(out_t[torch_index(ok)], ref[ok], "rows that do not read the bad page")
+
+
 def test_prefill_last_row_matches_decode_and_permutation():
     case = W.custom_case([150, 47], [150, 47], kind="prefill", block_size=16, seed=80)
     g = GpuCase(case)
