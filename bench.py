@@ -176,6 +176,8 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     part = pa.decode_partition_tokens(geom, n_dec, max_ctx_dec, partition) if n_dec else 0
     ws_bytes = pa.decode_workspace_bytes(geom, n_dec, max_ctx_dec, part) if n_dec else 0
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    pre_ws_bytes = pa.prefill_workspace_bytes(geom, n_pre, max_q, max_ctx_pre) if n_pre else 0
+    pre_ws = torch.empty(max(pre_ws_bytes, 1), dtype=torch.uint8, device=dev)
     out_dec = torch.empty((n_dec, 32, 64), dtype=torch.bfloat16, device=dev)
     out_pre = torch.empty((int(base.q_lens_prefill.sum()), 32, 64), dtype=torch.bfloat16,
                           device=dev)
@@ -198,7 +200,7 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
                     p0 = torch.cuda.Event(enable_timing=True)
                     p0.record(stream)
                 pa.prefill(geom, out_pre, L.q_pre, L.kp, L.vp, pre_bt, cu_q, pre_ctx, max_q,
-                           max_ctx_pre, scale, causal=True, stream=stream)
+                           max_ctx_pre, scale, causal=True, workspace=pre_ws, stream=stream)
             if n_dec:
                 if record:
                     d0 = torch.cuda.Event(enable_timing=True)
@@ -344,7 +346,8 @@ def main() -> int:
     if "prefill_ms" in res:
         ach = res["prefill_tflops"]
         key = "roofline_prefill" if "roofline" in line else "roofline"
-        line[key] = {"bound": "mfma", "kernel": "pa_prefill", "achieved": round(ach, 2),
+        line[key] = {"bound": "mfma", "kernel": "pa_prefill (prefill_kernel [+ prefill_merge_kernel when split])",
+                     "achieved": round(ach, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": hbm_traffic(args.workload + "-prefill" if key == "roofline_prefill"

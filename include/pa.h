@@ -191,19 +191,35 @@ int pa_decode(pa_geom_t g, void* out, const void* q, const void* k_pool, const v
  * ctx_lens[s] - q_len_s + i and sees keys 0..position (causal != 0) or all
  * ctx_lens[s] keys (causal == 0).  Keys before the chunk come from earlier appends,
  * so a chunk attends to the cached prefix.  Matrix products run on bf16 MFMA with fp32
- * accumulation.
+ * accumulation.  One workgroup per (tile of 32 query rows, sequence, KV head); when the
+ * call has fewer such tiles than two per compute unit, each tile's keys are split into
+ * pieces whose fp32 partials (max, sum, unnormalised output) a second kernel merges by
+ * log-sum-exp in piece order.
  *   out, q      [n_q_tokens][num_q_heads][head_dim] bf16 (device),
  *               n_q_tokens = cu_q_lens[n_seqs]
  *   cu_q_lens   int32 [n_seqs+1] (device); q_len_s <= ctx_lens[s] required
- *   max_q_len   host upper bound of q_len_s (sizes the grid)
+ *   max_q_len   host upper bound of q_len_s (sizes the grid: rows past it are not written)
  *   max_ctx_len host upper bound of ctx_lens (<= max_blocks_per_seq * block_size)
  *   scale       as for pa_decode: finite and > 0
+ *   kv_splits   0: automatic (1 when the grid has at least two tiles per compute unit of
+ *               the current device, else enough pieces for that, at most 8 and at most
+ *               ceil(max_ctx_len/64)); else that many pieces, 1 .. 8.  Other values give
+ *               PA_ERR_INVALID_ARG.
+ *   workspace   device scratch of at least pa_prefill_workspace_bytes(...) bytes for the
+ *               same arguments (on the same device); may be NULL when that size is 0.
+ *               With T = ceil(max_q_len/32) * n_seqs * num_kv_heads tiles and P pieces
+ *               it is T * P * 4 * 32 * (64 * 4 + 8) bytes, or 0 when P = 1.  Its
+ *               contents need no initialisation and are scratch after the call;
+ *               concurrent calls need separate workspaces.
+ * ceil(max_q_len/32) * n_seqs * num_kv_heads * 8 must stay below 2^31.
  * ------------------------------------------------------------------------------- */
+size_t pa_prefill_workspace_bytes(pa_geom_t g, int32_t n_seqs, int32_t max_q_len,
+                                  int32_t max_ctx_len, int32_t kv_splits);
 int pa_prefill(pa_geom_t g, void* out, const void* q, const void* k_pool, const void* v_pool,
                const int32_t* block_tables, int32_t max_blocks_per_seq,
                const int32_t* cu_q_lens, const int32_t* ctx_lens, int32_t n_seqs,
                int32_t max_q_len, int32_t max_ctx_len, float scale, int32_t causal,
-               void* stream);
+               int32_t kv_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,8 @@ from . import _lib
 
 __all__ = [
     "PagedAttnError", "Geometry", "PagePool", "page_bytes", "kv_append",
-    "decode_partition_tokens", "decode_workspace_bytes", "decode", "prefill", "library",
+    "decode_partition_tokens", "decode_workspace_bytes", "decode", "prefill_workspace_bytes",
+    "prefill", "library",
 ]
 
 
@@ -211,10 +212,18 @@ def decode(geom: Geometry, out, q, k_pool, v_pool, block_tables, ctx_lens, max_c
     _check(st, "pa_decode")
 
 
+def prefill_workspace_bytes(geom: Geometry, n_seqs: int, max_q_len: int, max_ctx_len: int,
+                            kv_splits: int = 0) -> int:
+    return int(_lib.load().pa_prefill_workspace_bytes(geom.c(), n_seqs, max_q_len, max_ctx_len,
+                                                      kv_splits))
+
+
 def prefill(geom: Geometry, out, q, k_pool, v_pool, block_tables, cu_q_lens, ctx_lens,
             max_q_len: int, max_ctx_len: int, scale: float, causal: bool = True,
-            stream=None) -> None:
-    """Packed query rows over their sequences' paged contexts (see pa_prefill)."""
+            kv_splits: int = 0, workspace=None, stream=None) -> None:
+    """Packed query rows over their sequences' paged contexts (see pa_prefill).
+    ``workspace`` is a uint8 device tensor of at least ``prefill_workspace_bytes`` bytes
+    (allocated here when omitted)."""
     import torch
 
     n = int(ctx_lens.numel())
@@ -228,8 +237,16 @@ def prefill(geom: Geometry, out, q, k_pool, v_pool, block_tables, cu_q_lens, ctx
     _dev(cu_q_lens, "cu_q_lens", torch.int32, n + 1)
     _dev(ctx_lens, "ctx_lens", torch.int32, n)
     _need(block_tables.shape[0] == n, "block_tables rows != n_seqs")
+    need = prefill_workspace_bytes(geom, n, int(max_q_len), int(max_ctx_len), int(kv_splits))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
     st = _lib.load().pa_prefill(geom.c(), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool),
                                 _ptr(block_tables), int(block_tables.shape[1]), _ptr(cu_q_lens),
                                 _ptr(ctx_lens), n, int(max_q_len), int(max_ctx_len), float(scale),
-                                1 if causal else 0, _stream(stream))
+                                1 if causal else 0, int(kv_splits), _ptr(workspace), ws_bytes,
+                                _stream(stream))
     _check(st, "pa_prefill")

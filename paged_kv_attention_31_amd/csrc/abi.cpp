@@ -55,6 +55,19 @@ int decode_args_ok(const pa_geom_t& g, int32_t n_seqs, int32_t max_ctx_len,
   return PA_OK;
 }
 
+// Host-checkable prefill arguments shared by the sizing and launch entry points.
+int prefill_args_ok(const pa_geom_t& g, int32_t n_seqs, int32_t max_q_len, int32_t max_ctx_len,
+                    int32_t kv_splits) {
+  int st = pa_geom_check(g);
+  if (st != PA_OK) return st;
+  if (n_seqs < 0 || max_q_len < 0 || max_ctx_len < 0) return PA_ERR_INVALID_ARG;
+  if (kv_splits < 0 || kv_splits > pa::kPrefillMaxSplit) return PA_ERR_INVALID_ARG;
+  // the grid (tiles x sequences x heads x pieces) must fit one launch dimension
+  if (ceil_div(max_q_len, 32) * n_seqs * g.num_kv_heads * pa::kPrefillMaxSplit > (int64_t)INT32_MAX)
+    return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------
@@ -229,25 +242,36 @@ int pa_decode(pa_geom_t g, void* out, const void* q, const void* k_pool, const v
                                       workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t pa_prefill_workspace_bytes(pa_geom_t g, int32_t n_seqs, int32_t max_q_len,
+                                  int32_t max_ctx_len, int32_t kv_splits) {
+  if (prefill_args_ok(g, n_seqs, max_q_len, max_ctx_len, kv_splits) != PA_OK) return 0;
+  return pa::plan_prefill(n_seqs, max_q_len, max_ctx_len, g.num_kv_heads, kv_splits,
+                          compute_units())
+      .ws_bytes;
+}
+
 int pa_prefill(pa_geom_t g, void* out, const void* q, const void* k_pool, const void* v_pool,
                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
                const int32_t* ctx_lens, int32_t n_seqs, int32_t max_q_len, int32_t max_ctx_len,
-               float scale, int32_t causal, void* stream) {
-  int st = pa_geom_check(g);
+               float scale, int32_t causal, int32_t kv_splits, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const int st = prefill_args_ok(g, n_seqs, max_q_len, max_ctx_len, kv_splits);
   if (st != PA_OK) return st;
-  if (n_seqs < 0 || max_blocks_per_seq <= 0 || max_q_len < 0 || max_ctx_len < 0)
-    return PA_ERR_INVALID_ARG;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
   if ((int64_t)max_ctx_len > (int64_t)max_blocks_per_seq * g.block_size) return PA_ERR_INVALID_ARG;
   if (max_q_len > max_ctx_len) return PA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return PA_ERR_INVALID_ARG;
   if (n_seqs == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !cu_q_lens || !ctx_lens)
     return PA_ERR_INVALID_ARG;
-  if ((int64_t)ceil_div(max_q_len, 32) * n_seqs * g.num_kv_heads > (int64_t)INT32_MAX)
-    return PA_ERR_INVALID_ARG;
-  return hip_status(pa::launch_prefill(to_launch(g), out, q, k_pool, v_pool, block_tables,
+  const pa::PrefillPlan plan = pa::plan_prefill(n_seqs, max_q_len, max_ctx_len, g.num_kv_heads,
+                                                kv_splits, compute_units());
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes))
+    return PA_ERR_WORKSPACE;
+  return hip_status(pa::launch_prefill(to_launch(g), plan, out, q, k_pool, v_pool, block_tables,
                                        max_blocks_per_seq, cu_q_lens, ctx_lens, n_seqs, max_q_len,
-                                       scale, causal, static_cast<hipStream_t>(stream)));
+                                       scale, causal, workspace,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

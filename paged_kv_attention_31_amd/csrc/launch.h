@@ -48,9 +48,25 @@ hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* ou
                          int max_blocks, const int32_t* ctx_lens, int n_seqs, int max_ctx_len,
                          float scale, void* workspace, hipStream_t stream);
 
-hipError_t launch_prefill(const LaunchGeom& geo, void* out, const void* q, const void* k_pool,
-                          const void* v_pool, const int32_t* block_tables, int max_blocks,
-                          const int32_t* cu_q_lens, const int32_t* ctx_lens, int n_seqs,
-                          int max_q_len, float scale, int causal, hipStream_t stream);
+// Prefill: one workgroup per (query tile of 32, sequence, KV head); when that gives fewer
+// than two workgroups per compute unit the tile's keys are split into up to
+// kPrefillMaxSplit pieces whose fp32 partials a merge kernel combines.
+constexpr int kPrefillMaxSplit = 8;
+
+struct PrefillPlan {
+  int64_t items;    // tiles x sequences x KV heads (the tile grid, ceil(max_q/32) tiles each)
+  int split;        // key pieces per tile (1: no merge)
+  size_t ws_bytes;  // partials (0 when split is 1)
+};
+
+// kv_splits 0: automatic; else that many pieces (1 .. kPrefillMaxSplit).
+PrefillPlan plan_prefill(int n_seqs, int max_q_len, int max_ctx_len, int num_kv_heads,
+                         int kv_splits, int compute_units);
+
+hipError_t launch_prefill(const LaunchGeom& geo, const PrefillPlan& plan, void* out, const void* q,
+                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                          int max_blocks, const int32_t* cu_q_lens, const int32_t* ctx_lens,
+                          int n_seqs, int max_q_len, float scale, int causal, void* workspace,
+                          hipStream_t stream);
 
 }  // namespace pa

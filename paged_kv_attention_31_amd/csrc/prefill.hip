@@ -43,6 +43,8 @@ constexpr int kQTile = 32;   // query positions per workgroup
 constexpr int kStage = 64;   // keys per LDS stage
 constexpr int kThreads = 256;
 constexpr float kLazy = 8.f;  // log2 of the largest p the lazy rescale lets through
+constexpr int kSlotFloats = kGroup * kQTile * kHeadDim;  // one partial output (fp32)
+constexpr int kSlotRows = kGroup * kQTile;               // (max, sum) pairs of one partial
 
 // Own value and the value of lane j ^ 32 (the two half-waves hold the same query's
 // keys), in either order, from one v_permlane32_swap (it exchanges the upper half of its
@@ -86,7 +88,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks,
     const int32_t* __restrict__ cu_q_lens, const int32_t* __restrict__ ctx_lens, int n_seqs,
-    int n_qtiles, int num_pages, int num_kv_heads, float qk_scale, int causal) {
+    int n_qtiles, int num_pages, int num_kv_heads, float qk_scale, int causal, int n_split,
+    float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
   using Lds = PrefillLds<BS>;
   constexpr int PPS = Lds::PPS;
   constexpr int VROW = Lds::VROW;
@@ -98,10 +101,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   // the XCDs (bid mod 8) and, inside one, to its shader engines in turn; without the
   // rotation a sequence would land on the same engine at every level and the engines'
   // loads would differ by the sequences' lengths.
+  // With n_split > 1 the tile's keys are cut into n_split pieces (pieces of one tile are
+  // n_split * Hkv workgroups apart; the KV head stays bid mod Hkv).
   const int bid = blockIdx.x;
   const int g = bid % num_kv_heads;
-  const int level = bid / (num_kv_heads * n_seqs);
-  const int s = ((bid / num_kv_heads) % n_seqs + level) % n_seqs;
+  const int piece = (bid / num_kv_heads) % n_split;
+  const int tb = bid / (num_kv_heads * n_split);  // tile-level position
+  const int level = tb / n_seqs;
+  const int s = (tb % n_seqs + level) % n_seqs;
   const int tile = n_qtiles - 1 - level;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -125,7 +132,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int pos_last = ctx - qlen + min(tile * kQTile + kQTile - 1, qlen - 1);
   const int kend = causal ? min(ctx, pos_last + 1) : ctx;    // keys [0, kend)
   const int klim = causal ? min(ctx, qpos + 1) : ctx;        // this lane's row sees keys < klim
-  const int n_stages = (kend + kStage - 1) / kStage;
+  const int n_all = (kend + kStage - 1) / kStage;       // stages of the whole tile
+  const int st0 = piece * n_all / n_split;              // this piece: stages st0 .. +n_stages
+  const int n_stages = (piece + 1) * n_all / n_split - st0;
   const int last_blk = kend > 0 ? (kend - 1) / BS : 0;
 
   // B operand of S^T = K.Q^T: lane (j, half) holds q[j][16*step + 8*half .. +8]
@@ -339,24 +348,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     }
   };
 
-  // Stage pipeline.  At iteration st: LDS buffer st % 2 holds stage st, the registers of
-  // stage st + 1 are in flight (issued an iteration ago), and the block-table entries of
-  // stage st + 2 have arrived.  The iteration issues the block-table loads of stage st + 3
-  // and the K/V loads of stage st + 2, computes stage st from LDS, stores stage st + 1
-  // to the other buffer and meets the barrier.  Every load is issued unconditionally
-  // (stages past the end are the cheap `live = false` kind) and the loop is unrolled by
-  // two with fixed registers per parity, so the compiler's wait counts let the loads of
-  // stage st + 2 stay in flight across the store of stage st + 1.
+  // Stage pipeline (stage indices relative to st0).  At iteration st: LDS buffer st % 2
+  // holds stage st, the registers of stage st + 1 are in flight (issued an iteration
+  // ago), and the block-table entries of stage st + 2 have arrived.  The iteration issues
+  // the block-table loads of stage st + 3 and the K/V loads of stage st + 2, computes
+  // stage st from LDS, stores stage st + 1 to the other buffer and meets the barrier.
+  // Every load is issued unconditionally (stages past the end are the cheap `live =
+  // false` kind) and the loop is unrolled by two with fixed registers per parity, so the
+  // compiler's wait counts let the loads of stage st + 2 stay in flight across the store
+  // of stage st + 1.
   StageRegs ra, rb;   // stage u lives in ra for even u, rb for odd u
   int pa_e, pb_e, pa_o, pb_o;  // block-table entries for even / odd stages
   if (n_stages > 0) {
     int p0a, p0b;
-    stage_pids(0, p0a, p0b);
-    stage_pids(1, pa_o, pb_o);
+    stage_pids(st0, p0a, p0b);
+    stage_pids(st0 + 1, pa_o, pb_o);
     stage_load(ra, p0a, p0b, true);
-    stage_pids(2, pa_e, pb_e);
+    stage_pids(st0 + 2, pa_e, pb_e);
     stage_load(rb, pa_o, pb_o, 1 < n_stages);
-    stage_store(ra, 0, 0);
+    stage_store(ra, st0, 0);
   }
   __syncthreads();
   // One iteration for stage st of parity P (0: st even).  Registers are chosen by name at
@@ -368,18 +378,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     const int buf = st & 1;
     // block-table entries of stage st + 3 (parity !P) ; K/V of stage st + 2 (parity P)
     if constexpr (P == 0) {
-      stage_pids(st + 3, pa_o, pb_o);
+      stage_pids(st0 + st + 3, pa_o, pb_o);
       stage_load(ra, pa_e, pb_e, st + 2 < n_stages);
     } else {
-      stage_pids(st + 3, pa_e, pb_e);
+      stage_pids(st0 + st + 3, pa_e, pb_e);
       stage_load(rb, pa_o, pb_o, st + 2 < n_stages);
     }
-    compute_stage(buf, st * kStage);
+    compute_stage(buf, (st0 + st) * kStage);
     if (st + 1 < n_stages) {
       if constexpr (P == 0)
-        stage_store(rb, st + 1, buf ^ 1);
+        stage_store(rb, st0 + st + 1, buf ^ 1);
       else
-        stage_store(ra, st + 1, buf ^ 1);
+        stage_store(ra, st0 + st + 1, buf ^ 1);
     }
     __syncthreads();
   };
@@ -387,6 +397,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     iteration(st, std::integral_constant<int, 0>{});
     if (st + 1 >= n_stages) break;
     iteration(st + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (n_split > 1) {
+    // a piece: fp32 partial (reference maximum, sum, unnormalised output) for the merge,
+    // slot (item, piece) with item = (tile * n_seqs + s) * Hkv + g, in lane order: wave w's
+    // accumulator chunk r (o0 then o1, 4 floats) of lane l at float (w * 8 + r) * 256 + 4 l,
+    // so every store (and the merge's load) moves one contiguous kilobyte
+    const float ltot = pair_sum(lsum);
+    const size_t slot = ((size_t)(tile * n_seqs + s) * num_kv_heads + g) * n_split + piece;
+    float* po = ws_o + slot * kSlotFloats + w * 8 * 256 + 4 * lane;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      *reinterpret_cast<f32x4_t*>(po + r4 * 256) =
+          f32x4_t{o0[4 * r4], o0[4 * r4 + 1], o0[4 * r4 + 2], o0[4 * r4 + 3]};
+      *reinterpret_cast<f32x4_t*>(po + (4 + r4) * 256) =
+          f32x4_t{o1[4 * r4], o1[4 * r4 + 1], o1[4 * r4 + 2], o1[4 * r4 + 3]};
+    }
+    if (half == 0) ws_ml[slot * kSlotRows + w * kQTile + j] = make_float2(m, ltot);
+    return;
   }
 
   // ---- normalise and store: lane holds dims 8*(r/4) + 4*half + (r%4) of query j ----------
@@ -406,28 +435,136 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   }
 }
 
+// Merge of a split tile: one wave per (item, head), item = (tile * n_seqs + s) * Hkv + g;
+// lane (j, half) holds the same dims as the split kernel wrote (its lane-ordered chunks).  The pieces combine by log-sum-exp in
+// piece order: M = max m_p, out = sum 2^(m_p - M) o_p / sum 2^(m_p - M) l_p; all pieces'
+// loads are issued before any is used.  A NaN piece (a row that saw an out-of-range
+// page) stays NaN.
+template <int NS>
+__global__ __launch_bounds__(64) void prefill_merge_kernel(
+    uint16_t* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
+    const int32_t* __restrict__ cu_q_lens, int n_seqs, int num_kv_heads) {
+  const int item = blockIdx.x / kGroup;  // one single-wave workgroup per (item, head)
+  const int w = blockIdx.x % kGroup;
+  const int g = item % num_kv_heads;
+  const int s = (item / num_kv_heads) % n_seqs;
+  const int tile = item / (num_kv_heads * n_seqs);
+  const int lane = threadIdx.x;
+  const int j = lane & 31;
+  const int half = lane >> 5;
+  const size_t slot0 = (size_t)item * NS;
+  float2 ml[NS];
+  f32x4_t x[NS][8];
+#pragma unroll
+  for (int p = 0; p < NS; ++p) {
+    ml[p] = ws_ml[(slot0 + p) * kSlotRows + w * kQTile + j];
+    const float* po = ws_o + (slot0 + p) * kSlotFloats + w * 8 * 256 + 4 * lane;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[p][r] = *reinterpret_cast<const f32x4_t*>(po + r * 256);
+  }
+  const int qa = cu_q_lens[s];
+  const int qlen = cu_q_lens[s + 1] - qa;
+  const int qi = tile * kQTile + j;
+  if (qi >= qlen) return;
+  float mx = kNegInf;
+#pragma unroll
+  for (int p = 0; p < NS; ++p) mx = vmax(mx, ml[p].x);
+  float acc[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+  float lt = 0.f;
+  if (mx != kNegInf) {
+#pragma unroll
+    for (int p = 0; p < NS; ++p) {
+      const float wgt = fast_exp2(ml[p].x - mx);  // 0 for a piece without visible keys
+      lt += wgt * ml[p].y;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * r + e] += wgt * x[p][r][e];
+    }
+  }
+  const float inv = lt == 0.f ? 0.f : 1.f / lt;
+  const int hq = num_kv_heads * kGroup;
+  // acc[4 r + e] is dim 8 (r % 4) + 4 half + e, + 32 for r >= 4 (the o0 / o1 order)
+  uint16_t* op = out + ((size_t)(qa + qi) * hq + g * kGroup + w) * kHeadDim + 4 * half;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    uint2 v;
+    v.x = pack_bf16x2(acc[4 * r + 0] * inv, acc[4 * r + 1] * inv);
+    v.y = pack_bf16x2(acc[4 * r + 2] * inv, acc[4 * r + 3] * inv);
+    *reinterpret_cast<uint2*>(op + (r < 4 ? 8 * r : 32 + 8 * (r - 4))) = v;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_prefill(const LaunchGeom& geo, void* out, const void* q, const void* k_pool,
-                          const void* v_pool, const int32_t* block_tables, int max_blocks,
-                          const int32_t* cu_q_lens, const int32_t* ctx_lens, int n_seqs,
-                          int max_q_len, float scale, int causal, hipStream_t stream) {
+PrefillPlan plan_prefill(int n_seqs, int max_q_len, int max_ctx_len, int num_kv_heads,
+                         int kv_splits, int compute_units) {
+  PrefillPlan p{};
+  const int64_t items = (int64_t)((max_q_len + kQTile - 1) / kQTile) * n_seqs * num_kv_heads;
+  const int64_t stages = std::max<int64_t>(1, ((int64_t)max_ctx_len + kStage - 1) / kStage);
+  p.items = items;
+  int64_t split = kv_splits;
+  if (split == 0) {  // enough workgroups for two per compute unit, at most 8 pieces
+    const int64_t want = 2 * (int64_t)std::max(compute_units, 1);
+    split = items > 0 && items < want ? (want + items - 1) / items : 1;
+    split = std::min<int64_t>(std::min<int64_t>(split, kPrefillMaxSplit), stages);
+  }
+  p.split = (int)std::max<int64_t>(split, 1);
+  if (p.split > 1)
+    p.ws_bytes = (size_t)items * p.split * (kSlotFloats * sizeof(float) + kSlotRows * sizeof(float2));
+  return p;
+}
+
+hipError_t launch_prefill(const LaunchGeom& geo, const PrefillPlan& plan, void* out, const void* q,
+                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                          int max_blocks, const int32_t* cu_q_lens, const int32_t* ctx_lens,
+                          int n_seqs, int max_q_len, float scale, int causal, void* workspace,
+                          hipStream_t stream) {
   const int n_qtiles = (max_q_len + kQTile - 1) / kQTile;
-  const dim3 grid((unsigned)((size_t)n_qtiles * n_seqs * geo.num_kv_heads));
+  const int ns = plan.split;
+  const dim3 grid((unsigned)(plan.items * ns));
   const dim3 block(kThreads);
   const float qk_scale = scale * kLog2e;
   auto* o = static_cast<uint16_t*>(out);
   auto* qq = static_cast<const uint16_t*>(q);
   auto* kp = static_cast<const uint16_t*>(k_pool);
   auto* vp = static_cast<const uint16_t*>(v_pool);
+  float* ws_o = nullptr;
+  float2* ws_ml = nullptr;
+  if (ns > 1) {
+    ws_o = static_cast<float*>(workspace);
+    ws_ml = reinterpret_cast<float2*>(ws_o + (size_t)plan.items * ns * kSlotFloats);
+  }
   if (geo.block_size == 16) {
     hipLaunchKernelGGL(prefill_kernel<16>, grid, block, 0, stream, o, qq, kp, vp, block_tables,
                        max_blocks, cu_q_lens, ctx_lens, n_seqs, n_qtiles, geo.num_pages,
-                       geo.num_kv_heads, qk_scale, causal);
+                       geo.num_kv_heads, qk_scale, causal, ns, ws_o, ws_ml);
   } else {
     hipLaunchKernelGGL(prefill_kernel<32>, grid, block, 0, stream, o, qq, kp, vp, block_tables,
                        max_blocks, cu_q_lens, ctx_lens, n_seqs, n_qtiles, geo.num_pages,
-                       geo.num_kv_heads, qk_scale, causal);
+                       geo.num_kv_heads, qk_scale, causal, ns, ws_o, ws_ml);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  const dim3 mgrid((unsigned)(plan.items * kGroup));
+  switch (ns) {
+#define PA_MERGE_CASE(N)                                                                    \
+  case N:                                                                                   \
+    hipLaunchKernelGGL(prefill_merge_kernel<N>, mgrid, dim3(64), 0, stream, o, ws_o, ws_ml, \
+                       cu_q_lens, n_seqs, geo.num_kv_heads);                                \
+    break;
+    PA_MERGE_CASE(2)
+    PA_MERGE_CASE(3)
+    PA_MERGE_CASE(4)
+    PA_MERGE_CASE(5)
+    PA_MERGE_CASE(6)
+    PA_MERGE_CASE(7)
+    PA_MERGE_CASE(8)
+#undef PA_MERGE_CASE
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -107,7 +107,7 @@ class GpuCase:
                   c.scale, partition_tokens=partition_tokens)
         return out
 
-    def prefill(self, causal: bool = True):
+    def prefill(self, causal: bool = True, kv_splits: int = 0):
         import paged_kv_attention_31_amd as pa
 
         t = torch_mod()
@@ -117,7 +117,7 @@ class GpuCase:
         r = c.prefill_seqs
         pa.prefill(self.geom, out, self.q_pre, self.kp, self.vp, self.pre_bt, self.cu_q,
                    self.pre_ctx, int(ql.max()), int(c.ctx_lens[r.start:r.stop].max()), c.scale,
-                   causal=causal)
+                   causal=causal, kv_splits=kv_splits)
         return out
 
 

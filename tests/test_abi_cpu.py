@@ -182,13 +182,45 @@ def test_partition_choice(lib):
         assert lib.pa_decode_workspace_bytes(g, n, ctx, part) == _plan_ws(n, ctx, 8, part)
 
 
+def _prefill_ws(n_seqs, max_q, max_ctx, hkv, splits, cus=256):
+    """Workspace bytes of the documented prefill plan (no device here: 256 compute units)."""
+    items = -(-max_q // 32) * n_seqs * hkv
+    stages = max(1, -(-max_ctx // 64))
+    p = splits
+    if p == 0:
+        want = 2 * cus
+        p = -(-want // items) if 0 < items < want else 1
+        p = min(p, 8, stages)
+    p = max(p, 1)
+    return 0 if p == 1 else items * p * 4 * 32 * (64 * 4 + 8)
+
+
+def test_prefill_workspace_bytes(lib):
+    g = geom()
+    for n, mq, mc, sp in ((8, 1024, 1024, 0), (1, 512, 1024, 0), (2, 32, 64, 0), (1, 1, 1, 0),
+                          (3, 100, 300, 3), (5, 40, 40, 1), (0, 32, 64, 0), (4, 0, 64, 0),
+                          (1, 64, 4096, 0), (64, 2048, 2048, 0)):
+        assert lib.pa_prefill_workspace_bytes(g, n, mq, mc, sp) == _prefill_ws(n, mq, mc, 8, sp)
+    assert lib.pa_prefill_workspace_bytes(g, 2, 32, 64, -1) == 0  # invalid: nothing to size
+
+
 def test_prefill_and_append_validation(lib):
     g = geom()
     pf = lambda **k: lib.pa_prefill(k.get("g", g), k.get("out", FAKE), FAKE, FAKE, FAKE, FAKE,
                                     k.get("max_blocks", 4), FAKE, FAKE, k.get("n", 2),
                                     k.get("max_q", 32), k.get("max_ctx", 64),
-                                    k.get("scale", 0.125), 1, None)
+                                    k.get("scale", 0.125), 1, k.get("splits", 1),
+                                    k.get("ws", None), k.get("ws_bytes", 0), None)
     assert pf(out=None) == _lib.PA_ERR_INVALID_ARG
+    assert pf(splits=-1) == _lib.PA_ERR_INVALID_ARG
+    assert pf(splits=9) == _lib.PA_ERR_INVALID_ARG
+    # a split call needs the partial workspace; an unsplit one none
+    assert pf(splits=2) == _lib.PA_ERR_WORKSPACE
+    need = lib.pa_prefill_workspace_bytes(g, 2, 32, 64, 2)
+    assert need == _prefill_ws(2, 32, 64, 8, 2)
+    assert pf(splits=2, ws=FAKE, ws_bytes=need - 1) == _lib.PA_ERR_WORKSPACE
+    # the grid (tiles x sequences x heads x 8 pieces) must fit a launch dimension
+    assert pf(n=1 << 15, max_q=32768, max_ctx=32768, max_blocks=2048) == _lib.PA_ERR_INVALID_ARG
     assert pf(scale=0.0) == _lib.PA_ERR_INVALID_ARG
     assert pf(scale=-1.0) == _lib.PA_ERR_INVALID_ARG
     assert pf(scale=float("inf")) == _lib.PA_ERR_INVALID_ARG

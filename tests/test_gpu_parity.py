@@ -256,7 +256,23 @@ def test_prefill_chunked_ragged(bs, causal):
     assert_close(out, ref, f"prefill bs={bs} causal={causal}")
 
 
-def test_prefill_out_of_range_page_gives_nan_rows():
+@pytest.mark.parametrize("splits", [1, 2, 5, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_key_splits(splits, causal):
+    # each tile's keys cut into pieces merged by log-sum-exp (pieces shorter than a stage
+    # stay empty), against the same call unsplit and the oracle
+    case = W.custom_case([70, 33, 129, 1, 200, 64, 300], [7, 33, 100, 1, 1, 40, 300],
+                         kind="prefill", block_size=16, seed=90)
+    _announce(f"prefill kv_splits={splits} causal={causal}")
+    g = GpuCase(case)
+    out = g.prefill(causal=causal, kv_splits=splits)
+    kp, vp = oracle_pools(case)
+    ref = oracle_prefill(case, kp, vp, causal=causal)
+    assert_close(out, ref, f"prefill kv_splits={splits} causal={causal}")
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_prefill_out_of_range_page_gives_nan_rows(splits):
     # a block-table entry outside the pool: exactly the rows whose keys reach that block
     # come out NaN (every head), the others match the oracle
     case = W.custom_case([200, 90], [200, 90], kind="prefill", block_size=16, seed=91)
@@ -268,7 +284,7 @@ def test_prefill_out_of_range_page_gives_nan_rows():
     bt[0, blk] = case.num_pages + 3
     from tests.gpu_helpers import i32_dev
     g.pre_bt = i32_dev(bt)
-    out_t = g.prefill()
+    out_t = g.prefill(kv_splits=splits)
     out = out_t.float().cpu().numpy()
     pos = np.arange(200)  # sequence 0 is a whole prompt: row i sits at position i
     sees = pos >= blk * 16
