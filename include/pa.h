@@ -167,8 +167,8 @@ int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool
  *   workspace       device scratch of at least pa_decode_workspace_bytes(...) bytes
  *                   for the same arguments (on the same device); may be NULL when that
  *                   size is 0.  With W workers and S = n_seqs * num_kv_heads + W it is
- *                   S * 4 * (64 * 4 + 8) + 8 * W bytes (fp32 partials, then two int32
- *                   lists of W), or 0 when no pair can be split (ceil(max_ctx_len/64) <= 1
+ *                   S * 4 * (64 * 4 + 8) + 8 * (W + 1) bytes (fp32 partials, then W + 1
+ *                   int32 pairs), or 0 when no pair can be split (ceil(max_ctx_len/64) <= 1
  *                   or W = 1).  Its contents need no initialisation and are scratch
  *                   after the call; concurrent calls need separate workspaces.
  * pa_decode_partition_tokens returns the most tokens one worker streams for these

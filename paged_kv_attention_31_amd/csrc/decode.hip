@@ -107,6 +107,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   __shared__ int wsum_sh[kDecodeWaves];
   __shared__ uint4 q_sh[kDecodeWaves][2][kGroup][8];  // [wave][slot][head][piece]
   __shared__ __attribute__((aligned(16))) uint16_t p_sh[kDecodeWaves][kGroup][64];
+  __shared__ __attribute__((aligned(16))) float fin_sh[kDecodeWaves][kGroup * kHeadDim];
+  __shared__ float2 fin_ml[kDecodeWaves][kGroup];
 
   // ---- 1. tiles per sequence and their exclusive prefix sum over 256 chunks -----------
   const int chunk = (n_seqs + 255) / 256;
@@ -135,6 +137,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   const bool has_ws = ws_desc != nullptr;
   const int64_t n_tiles = (int64_t)uni(scan_sh[256]) * hkv;
   const int64_t n_eff = min((int64_t)n_workers, n_tiles);
+  // header for the merge: stream length and the number of waves it is cut into
+  if (has_ws && wid == 0 && lane == 0) ws_desc[n_workers] = make_int2((int)n_tiles, (int)n_eff);
   if (wid >= n_eff) {
     if (has_ws && lane == 0) ws_desc[wid] = make_int2(-1, 0);
     return;
@@ -362,8 +366,18 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   // first tile of a cut segment (its last segment) records (segment, number of covering
   // waves) for the merge; wave(t) = floor(((t + 1) * n_eff - 1) / n_tiles) is the range
   // holding stream tile t.
+  // The result goes through LDS so that one 16-byte store per lane writes it (bf16: lane
+  // l < 32 holds head l / 8, dims 8 (l % 8) .. +8; fp32: lane l holds head l / 16, dims
+  // 4 (l % 16) .. +4), and the stores themselves are issued by the step on every tile
+  // through buffer descriptors whose range is empty unless a segment ended: equal store
+  // counts on every path keep the compiler's vector-memory wait counts exact, so the K/V
+  // loads in flight are never waited on because of these stores.  The data they store is
+  // left in acc[0][0..3] and acc[1][0..1] (reset right after).
+  constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3: raw (untyped) access
+  auto rsrc_none = [&]() { return __builtin_amdgcn_make_buffer_rsrc(out, 0, 0, kRsrcWord3); };
   int2 own = make_int2(-1, 0);
-  auto finish = [&](const Cursor& c, bool started, bool whole, bool bad) {
+  auto finish = [&](const Cursor& c, bool started, bool whole, bool bad,
+                    __amdgpu_buffer_rsrc_t& r_data, __amdgpu_buffer_rsrc_t& r_ml) {
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
       l[h] = wave_sum(l[h]);
@@ -375,43 +389,71 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
         acc[i][h] = bad ? __builtin_nanf("") : a;
       }
     }
+    // lanes l % LPR == 0 hold dims l / LPR + i * RPI of every head
+    if (lane % LPR == 0) {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) fin_sh[w][h * kHeadDim + lane / LPR + i * RPI] = acc[i][h];
+    }
+    // m and l are wave-uniform
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) fin_ml[w][h] = make_float2(m[h], l[h]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int seg = c.s * hkv + c.g;
     if (whole) {
-      if (lane % LPR == 0) {
-#pragma unroll
-        for (int h = 0; h < kGroup; ++h) {
-          const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
-          uint16_t* o = out + ((size_t)c.s * hq + c.g * kGroup + h) * kHeadDim + lane / LPR;
-#pragma unroll
-          for (int i = 0; i < NV; ++i) o[i * RPI] = to_bf16(acc[i][h] * inv);
-        }
-      }
+      // lane l < 32: head l / 8, dims 8 (l % 8) .. +8
+      const int lw = lane & 31;
+      const f32x4_t f0 = *reinterpret_cast<const f32x4_t*>(&fin_sh[w][8 * lw]);
+      const f32x4_t f1 = *reinterpret_cast<const f32x4_t*>(&fin_sh[w][8 * lw + 4]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int hl = lw >> 3;
+      const float lh = hl == 0 ? l[0] : hl == 1 ? l[1] : hl == 2 ? l[2] : l[3];
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      acc[0][0] = __uint_as_float(pack_bf16x2(f0[0] * inv, f0[1] * inv));
+      acc[0][1] = __uint_as_float(pack_bf16x2(f0[2] * inv, f0[3] * inv));
+      acc[0][2] = __uint_as_float(pack_bf16x2(f1[0] * inv, f1[1] * inv));
+      acc[0][3] = __uint_as_float(pack_bf16x2(f1[2] * inv, f1[3] * inv));
+      // 512 bytes: lanes 32..63 fall outside and write nothing
+      r_data = __builtin_amdgcn_make_buffer_rsrc(
+          out + ((size_t)c.s * hq + c.g * kGroup) * kHeadDim, 0, kGroup * kHeadDim * 2, kRsrcWord3);
     } else {
-      if (started) {
-        const int64_t last_tile = c.first + (int64_t)c.g * c.nt + c.nt - 1;
-        const int w1 = (int)(((last_tile + 1) * n_eff - 1) / n_tiles);
-        own = make_int2(seg, w1 - wid + 1);
-      }
+      const f32x4_t f = *reinterpret_cast<const f32x4_t*>(&fin_sh[w][4 * lane]);
+      const float2 mlp = fin_ml[w][lane & 3];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // the owner records the stream index of the segment's last tile; the merge finds
+      // the wave holding it
+      if (started) own = make_int2(seg, (int)(c.first + (int64_t)c.g * c.nt + c.nt - 1));
       const size_t slot = (size_t)seg + wid;
-      if (lane % LPR == 0) {
-#pragma unroll
-        for (int h = 0; h < kGroup; ++h) {
-          float* o = ws_o + (slot * kGroup + h) * kHeadDim + lane / LPR;
-#pragma unroll
-          for (int i = 0; i < NV; ++i) o[i * RPI] = acc[i][h];
-        }
-      }
-      if (lane < kGroup) {
-        float mv = m[0], lv = l[0];
-#pragma unroll
-        for (int h = 1; h < kGroup; ++h) {
-          mv = lane == h ? m[h] : mv;
-          lv = lane == h ? l[h] : lv;
-        }
-        ws_ml[slot * kGroup + lane] = make_float2(mv, lv);
-      }
+      acc[0][0] = f[0];
+      acc[0][1] = f[1];
+      acc[0][2] = f[2];
+      acc[0][3] = f[3];
+      acc[1][0] = mlp.x;  // lanes 0..3: (m, l) of head lane
+      acc[1][1] = mlp.y;
+      r_data = __builtin_amdgcn_make_buffer_rsrc(ws_o + slot * kGroup * kHeadDim, 0,
+                                                 kGroup * kHeadDim * 4, kRsrcWord3);
+      // 32 bytes: lanes 4..63 fall outside and write nothing
+      r_ml = __builtin_amdgcn_make_buffer_rsrc(ws_ml + slot * kGroup, 0, kGroup * 8, kRsrcWord3);
     }
-    reset();
+  };
+  // the store slot of every tile (see above): 16 bytes of output or partial per lane, and
+  // (m, l) for lanes 0..3
+  auto store_slot = [&](__amdgpu_buffer_rsrc_t r_data, __amdgpu_buffer_rsrc_t r_ml) {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4_t{__float_as_uint(acc[0][0]), __float_as_uint(acc[0][1]), __float_as_uint(acc[0][2]),
+                __float_as_uint(acc[0][3])},
+        r_data, lane * 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(
+        u32x2_t{__float_as_uint(acc[1][0]), __float_as_uint(acc[1][1])}, r_ml, lane * 8, 0, 0);
   };
 
   // ---- 3. stream the range ------------------------------------------------------------
@@ -452,8 +494,12 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     bad_nxt = load_kv(nxt, c1, pid_n1, t + 1 < L);
     seg_bad |= bad_cur;
     compute(cur, cc, t & 1);
-    if (t == L - 1 || cc.i == cc.nt - 1) {
-      finish(cc, seg_whole, seg_whole && cc.i == cc.nt - 1, seg_bad);
+    const bool ends = t == L - 1 || cc.i == cc.nt - 1;
+    __amdgpu_buffer_rsrc_t r_data = rsrc_none(), r_ml = rsrc_none();
+    if (ends) finish(cc, seg_whole, seg_whole && cc.i == cc.nt - 1, seg_bad, r_data, r_ml);
+    store_slot(r_data, r_ml);
+    if (ends) {
+      reset();
       seg_whole = true;
       seg_bad = false;
     }
@@ -475,10 +521,12 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 
 // Combine the partials of every segment that range boundaries cut.  Wave wid's
 // descriptor names the segment it owns (it holds the segment's first tile) and the
-// number np of consecutive waves wid .. wid + np - 1 that left partials for it, in
-// slots seg + wid .. seg + wid + np - 1:  M = max_j m_j, L = sum_j l_j 2^(m_j - M),
-// out = sum_j o_j 2^(m_j - M) / L, the sums taken in ascending wave order.  Lane = head
-// dimension; the (m, l) pairs and the outputs are loaded lane-parallel.
+// stream index of the segment's last tile; with the header (stream length T, waves E)
+// the wave holding that tile is w1 = floor(((last + 1) E - 1) / T), so np = w1 - wid + 1
+// consecutive waves left partials for the segment, in slots seg + wid .. seg + w1:
+// M = max_j m_j, L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L, the sums
+// taken in ascending wave order.  Lane = head dimension; the (m, l) pairs and the
+// outputs are loaded lane-parallel.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
     const int2* __restrict__ ws_desc, int n_workers, int num_kv_heads) {
@@ -487,8 +535,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   if (wid >= n_workers) return;
   const int2 desc = ws_desc[wid];
   const int seg = desc.x;
-  const int np = desc.y;
-  if (seg < 0 || np < 2) return;
+  if (seg < 0) return;
+  const int2 hdr = ws_desc[n_workers];  // (tiles in the stream, workers)
+  const int w_last = (int)((((int64_t)desc.y + 1) * hdr.y - 1) / hdr.x);  // holds tile desc.y
+  const int np = w_last - wid + 1;
+  if (np < 2) return;
   const int s = seg / num_kv_heads;
   const int g = seg - s * num_kv_heads;
   const int hq = num_kv_heads * kGroup;
@@ -568,7 +619,7 @@ DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partit
   if (p.merge) {
     const int64_t slots = (int64_t)n_seqs * num_kv_heads + workers;
     p.ws_bytes = (size_t)slots * kGroup * (kHeadDim * sizeof(float) + sizeof(float2)) +
-                 (size_t)workers * sizeof(int2);
+                 (size_t)(workers + 1) * sizeof(int2);
   }
   return p;
 }

@@ -155,7 +155,7 @@ def _plan_ws(n_seqs, max_ctx, hkv, part, cus=256):
     workers = max(1, min(workers, n_max))
     if workers == 1 or tiles == 1:
         return 0
-    return (n_seqs * hkv + workers) * 4 * (64 * 4 + 8) + 2 * workers * 4
+    return (n_seqs * hkv + workers) * 4 * (64 * 4 + 8) + 8 * (workers + 1)
 
 
 def test_partition_choice(lib):
