@@ -152,31 +152,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 
   // ---- staging: thread t moves K chunks t, t+256 and V chunks t, t+256 of a stage ------
   // chunk c of a stage: page c / KCH, 16-byte piece c % KCH of that page's head slice.
-  // A thread's share of a stage: K and V chunks tid and tid + 256 (16 bytes each).
+  // A thread's share of a stage: K and V chunks tid and tid + 256 (16 bytes each).  A
+  // page slice is KCH >= 128 chunks, so each wave's 64 chunks of either kind lie in one
+  // page: block-table entries and page addresses are wave-uniform (scalar registers),
+  // and a lane only adds its byte offset within the page.
   struct StageRegs {  // plain vector types: HIP's uint4 copies go through the stack
     u32x4_t k0, k1, v0, v1;
-    int bad;  // bit 0 / 1: the page of chunk t / t + 256 was out of range
+    int bad;  // bit 0 / 1: the page of chunk t / t + 256 was out of range (wave-uniform)
   };
-  // Block-table entries of the pages holding the thread's two chunks of stage st, pages
-  // past the last needed block repeating it.
+  const int pj_a = (64 * w) / KCH;             // page (within a stage) of chunk tid
+  const int pj_b = (64 * w + kThreads) / KCH;  // and of chunk tid + 256
+  const unsigned off_a = (unsigned)(tid % KCH) * 16u;               // bytes into the page slice
+  const unsigned off_b = (unsigned)((tid + kThreads) % KCH) * 16u;
+  const size_t page_bytes = page_stride * sizeof(uint16_t);
+  const char* k_base = reinterpret_cast<const char*>(k_head);
+  const char* v_base = reinterpret_cast<const char*>(v_head);
+  // Block-table entries of the wave's two pages of stage st, pages past the last needed
+  // block repeating it.
   auto stage_pids = [&](int st, int& pa, int& pb) __attribute__((always_inline)) {
     const int blk0 = st * (kStage / BS);
-    pa = bt[min(blk0 + tid / KCH, last_blk)];
-    pb = bt[min(blk0 + (tid + kThreads) / KCH, last_blk)];
+    pa = bt[__builtin_amdgcn_readfirstlane(min(blk0 + pj_a, last_blk))];
+    pb = bt[__builtin_amdgcn_readfirstlane(min(blk0 + pj_b, last_blk))];
   };
   // Issue the thread's loads of a stage.  `live` false (a stage past the end) points every
-  // lane at one 16-byte piece, so each load instruction fetches one line.  A page id out
-  // of range reads page 0 instead and marks the chunk, which is staged as K = NaN, V = 0.
+  // lane at the page's first 16 bytes, so each load instruction fetches one line.  A page
+  // id out of range reads page 0 instead and marks the chunk, which is staged as K = NaN,
+  // V = 0.
   auto stage_load = [&](StageRegs& r, int pa, int pb, bool live) __attribute__((always_inline)) {
+    pa = __builtin_amdgcn_readfirstlane(pa);
+    pb = __builtin_amdgcn_readfirstlane(pb);
     r.bad = 0;
     if ((unsigned)pa >= (unsigned)num_pages) { r.bad |= 1; pa = 0; }
     if ((unsigned)pb >= (unsigned)num_pages) { r.bad |= 2; pb = 0; }
-    const size_t ba = (size_t)pa * page_stride + (live ? (size_t)(tid % KCH) * 8 : 0);
-    const size_t bb = (size_t)pb * page_stride + (live ? (size_t)((tid + kThreads) % KCH) * 8 : 0);
-    r.k0 = *reinterpret_cast<const u32x4_t*>(k_head + ba);
-    r.v0 = *reinterpret_cast<const u32x4_t*>(v_head + ba);
-    r.k1 = *reinterpret_cast<const u32x4_t*>(k_head + bb);
-    r.v1 = *reinterpret_cast<const u32x4_t*>(v_head + bb);
+    const size_t pga = (size_t)pa * page_bytes, pgb = (size_t)pb * page_bytes;
+    const unsigned oa = live ? off_a : 0u, ob = live ? off_b : 0u;
+    r.k0 = *reinterpret_cast<const u32x4_t*>(k_base + pga + oa);
+    r.v0 = *reinterpret_cast<const u32x4_t*>(v_base + pga + oa);
+    r.k1 = *reinterpret_cast<const u32x4_t*>(k_base + pgb + ob);
+    r.v1 = *reinterpret_cast<const u32x4_t*>(v_base + pgb + ob);
   };
   // V chunk c: dim row within / (BS/8), keys 8 * (within % (BS/8)) .. +8 of page c / KCH;
   // keys at or past the context end are cleared
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   // Rows that see a key of an out-of-range page get NaN scores (and so a NaN output);
   // V = 0 keeps the page's stale values out of the rows that mask those keys.
   auto stage_store = [&](StageRegs& r, int st, int buf) __attribute__((always_inline)) {
-    if (__builtin_expect(__ballot(r.bad != 0) != 0, 0)) {
+    if (__builtin_expect(r.bad != 0, 0)) {
       const u32x4_t nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
       const u32x4_t zero4 = {0u, 0u, 0u, 0u};
       if (r.bad & 1) { r.k0 = nan4; r.v0 = zero4; }
@@ -368,6 +381,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     stage_load(rb, pa_o, pb_o, 1 < n_stages);
     stage_store(ra, st0, 0);
   }
+  // An explicit use of q here, after the prologue has waited for younger loads: the
+  // compiler's wait counts then know q has arrived on every path into the loop, instead
+  // of waiting for it (and every load issued after it) at the top of each trip.
+  asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
   __syncthreads();
   // One iteration for stage st of parity P (0: st even).  Registers are chosen by name at
   // compile time (stage u lives in ra for even u, rb for odd u; the block-table entries of
@@ -385,19 +402,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
       stage_load(rb, pa_o, pb_o, st + 2 < n_stages);
     }
     compute_stage(buf, (st0 + st) * kStage);
-    if (st + 1 < n_stages) {
-      if constexpr (P == 0)
-        stage_store(rb, st0 + st + 1, buf ^ 1);
-      else
-        stage_store(ra, st0 + st + 1, buf ^ 1);
-    }
+    // Stored on every iteration, also past the last stage (the other buffer is not read
+    // again then): a store skipped on some paths would leave its loads pending at the loop
+    // back edge, and the compiler then waits for every load at the top of the loop.
+    if constexpr (P == 0)
+      stage_store(rb, st0 + st + 1, buf ^ 1);
+    else
+      stage_store(ra, st0 + st + 1, buf ^ 1);
     __syncthreads();
   };
-  for (int st = 0; st < n_stages; st += 2) {
+  // Pairs of stages, then an odd last stage alone: the loop has a single back edge and
+  // one exit, so the compiler's wait at the loop top covers only the block-table entries,
+  // not the K/V loads meant to stay in flight (an exit between the two halves made it
+  // wait for every load there).  The odd last stage has nothing left to load or store.
+  int st = 0;
+  for (; st + 1 < n_stages; st += 2) {
     iteration(st, std::integral_constant<int, 0>{});
-    if (st + 1 >= n_stages) break;
     iteration(st + 1, std::integral_constant<int, 1>{});
   }
+  if (st < n_stages) compute_stage(st & 1, (st0 + st) * kStage);
 
   if (n_split > 1) {
     // a piece: fp32 partial (reference maximum, sum, unnormalised output) for the merge,
