@@ -198,8 +198,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     const int within = c - pj * KCH;
     const int row = within / (BS / 8);
     const int c8 = within - row * (BS / 8);
-    const int key0 = k0 + pj * BS + c8 * 8;
-    if (tail && key0 + 8 > ctx) {
+    if (__builtin_expect(tail, 0)) {  // uniform: only the stage holding the context end
+      const int key0 = k0 + pj * BS + c8 * 8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         if (key0 + e >= ctx) vv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
@@ -228,7 +228,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
 
   // This lane's query row: reference maximum m (scaled), m + kLazy, the FMA addend -m (0
   // while m is -inf, so masked scores give 2^-inf = 0), and the running sum.
-  float m = kNegInf, mthr = kNegInf, negm = 0.f, lsum = 0.f;
+  float m = kNegInf, mthr = kNegInf, negm = 0.f, lsum = 0.f;  // mthr: raw-score units
+  const float inv_scale = 1.f / qk_scale;
   const int lim_lane = klim - 4 * half;  // key offsets from a half's base below this are visible
   f32x16_t o0 = {}, o1 = {};
 
@@ -272,22 +273,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     const float t2 = vmax3(sv[6], sv[7], sv[8]), t3 = vmax3(sv[9], sv[10], sv[11]);
     const float t4 = vmax3(sv[12], sv[13], sv[14]);
     float mt = vmax3(vmax3(t0, t1, t2), vmax(t3, t4), sv[15]);
-    mt = pair_max(mt) * qk_scale;  // scores are scaled by qk_scale > 0 below
+    mt = pair_max(mt);  // raw scores; scaled by qk_scale > 0 below
     // Lazy rescale: the running maximum m is only a reference point, any value works as
     // long as sums and outputs use the same one.  It is moved (and sums and outputs
     // rescaled) only when a row's new maximum exceeds it by more than 2^kLazy, so p stays
     // <= 2^kLazy and the rescale runs about once per row instead of nearly every tile.
     if (__ballot(mt > mthr)) {
-      const float mn = vmax(m, mt);
+      const float mn = vmax(m, mt * qk_scale);
       const float alpha = m == kNegInf ? 0.f : fast_exp2(m - mn);
-      lsum *= alpha;
+      if (__ballot(m != kNegInf)) {  // rows still at -inf hold o = 0, l = 0: nothing to scale
+        lsum *= alpha;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        o0[r] *= alpha;
-        o1[r] *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          o0[r] *= alpha;
+          o1[r] *= alpha;
+        }
       }
       m = mn;
-      mthr = m + kLazy;
+      mthr = (m + kLazy) * inv_scale;
       negm = m == kNegInf ? 0.f : -m;
     }
     // p = 2^(s * qk_scale - m), rounded to bf16 once: the P.V operand; the running sum
@@ -296,13 +299,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     for (int i = 0; i < 8; ++i)
       pk[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(sv[2 * i], qk_scale, negm)),
                           fast_exp2(__builtin_fmaf(sv[2 * i + 1], qk_scale, negm)));
-    float pa = 0.f, pb = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      pa = dot2(pk[i], 0x3F803F80u, pa);
-      pb = dot2(pk[i + 1], 0x3F803F80u, pb);
-    }
-    lsum += pa + pb;
+    for (int i = 0; i < 8; ++i) lsum = dot2(pk[i], 0x3F803F80u, lsum);
   };
   // O^T += V^T . P^T.  Element e (0..7) of lane half h's B operand for k-step ks is the
   // score of key 16 ks + (e < 4 ? 0 : 8) + 4 h + (e & 3) (the S^T accumulator order), so
