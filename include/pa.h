@@ -143,6 +143,34 @@ int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool
                  int32_t n_new_tokens, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * rope_kv_append ([guide] §Llama 3.2 1B架构拆解: rotary position encoding turns Q and K
+ * by the token's position before attention; §推理流程：从Prefill到Decode: K/V join the
+ * cache before the token attends).  For the same rows, positions and pages as
+ * pa_kv_append: K is rotated and appended, V is appended unchanged, and Q (when given)
+ * is rotated into q_out.  Pair i of a head vector is (x[i], x[i + head_dim/2]) and turns
+ * counter-clockwise by pos * f_i:  (a, b) -> (a cos t - b sin t, b cos t + a sin t),
+ * with f_i = rope_theta^(-2i/head_dim), or f_i = inv_freq[i] when inv_freq is given
+ * (any rescaled frequency table).  Angles are formed and reduced in fp64, the rotation
+ * runs in fp32 and each result is rounded once to bf16 (nearest even).
+ *   q, q_out        [n_new_tokens][num_q_heads][head_dim] bf16 (device); q_out may be
+ *                   q (in place); both NULL to rotate K only
+ *   k_new, v_new, block_tables, cu_new_lens, ctx_lens, n_seqs, n_new_tokens: as for
+ *                   pa_kv_append (positions ctx_lens[s] - n_s + j)
+ *   rope_theta      base of the frequency table (> 0, finite; 500000 for the Llama 3
+ *                   family); ignored when inv_freq is given
+ *   inv_freq        NULL or head_dim/2 fp32 frequencies (device)
+ * A row whose position falls outside its block-table row, or whose page id is out of
+ * range, is not appended (its Q is still rotated).  PA_ERR_INVALID_ARG for a missing
+ * pointer, exactly one of q / q_out NULL, or a bad rope_theta without inv_freq.
+ * ------------------------------------------------------------------------------- */
+int pa_rope_kv_append(pa_geom_t g, const void* q, void* q_out, const void* k_new,
+                      const void* v_new, void* k_pool, void* v_pool,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* cu_new_lens, const int32_t* ctx_lens, int32_t n_seqs,
+                      int32_t n_new_tokens, double rope_theta, const float* inv_freq,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Decode ([guide] §推理流程, §在线Softmax): one query row per sequence, the newest
  * token at position ctx_lens[s]-1, attending to all ctx_lens[s] keys (so the token's
  * own K/V must already be appended).  Every (sequence, KV head) pair is streamed once

@@ -21,7 +21,7 @@ from typing import Optional, Sequence
 from . import _lib
 
 __all__ = [
-    "PagedAttnError", "Geometry", "PagePool", "page_bytes", "kv_append",
+    "PagedAttnError", "Geometry", "PagePool", "page_bytes", "kv_append", "rope_kv_append",
     "decode_partition_tokens", "decode_workspace_bytes", "decode", "prefill_workspace_bytes",
     "prefill", "library",
 ]
@@ -166,6 +166,38 @@ def kv_append(geom: Geometry, k_new, v_new, k_pool, v_pool, block_tables, cu_new
                                   _ptr(block_tables), int(block_tables.shape[1]),
                                   _ptr(cu_new_lens), _ptr(ctx_lens), n_seqs, t, _stream(stream))
     _check(st, "pa_kv_append")
+
+
+def rope_kv_append(geom: Geometry, q, q_out, k_new, v_new, k_pool, v_pool, block_tables,
+                   cu_new_lens, ctx_lens, rope_theta: float = 500000.0, inv_freq=None,
+                   stream=None) -> None:
+    """Rotate the new rows' Q (into ``q_out``, which may be ``q``) and K by their
+    positions and append K and V to the pools (see pa_rope_kv_append).  ``q``/``q_out``
+    may both be None; ``inv_freq`` is None or head_dim/2 float32 frequencies."""
+    import torch
+
+    n_seqs = int(ctx_lens.numel())
+    t = int(k_new.shape[0]) if k_new.dim() > 0 else 0
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        _dev(x, name, torch.bfloat16, t * geom.num_kv_heads * geom.head_dim)
+    _need((q is None) == (q_out is None), "q and q_out must both be given or both be None")
+    if q is not None:
+        for name, x in (("q", q), ("q_out", q_out)):
+            _dev(x, name, torch.bfloat16, t * geom.num_q_heads * geom.head_dim)
+    if inv_freq is not None:
+        _dev(inv_freq, "inv_freq", torch.float32, geom.head_dim // 2)
+    for name, x in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(x, name, torch.bfloat16, geom.num_pages * geom.page_elems)
+    _dev(block_tables, "block_tables", torch.int32, dims=2)
+    _dev(cu_new_lens, "cu_new_lens", torch.int32, n_seqs + 1)
+    _dev(ctx_lens, "ctx_lens", torch.int32, n_seqs)
+    _need(block_tables.shape[0] == n_seqs, "block_tables rows != n_seqs")
+    st = _lib.load().pa_rope_kv_append(
+        geom.c(), _ptr(q), _ptr(q_out),
+        _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(cu_new_lens), _ptr(ctx_lens), n_seqs, t,
+        float(rope_theta), _ptr(inv_freq), _stream(stream))
+    _check(st, "pa_rope_kv_append")
 
 
 def decode_partition_tokens(geom: Geometry, n_seqs: int, max_ctx_len: int,

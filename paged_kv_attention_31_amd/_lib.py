@@ -46,6 +46,9 @@ SIGNATURES = {
     "pa_pool_refcount": (_c_i32, [_c_p, _c_i32]),
     "pa_kv_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p,
                                     _c_i32, _c_i32, _c_p]),
+    "pa_rope_kv_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                         _c_i32, _c_p, _c_p, _c_i32, _c_i32, ctypes.c_double,
+                                         _c_p, _c_p]),
     "pa_decode_partition_tokens": (_c_i32, [PaGeom, _c_i32, _c_i32, _c_i32]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [PaGeom, _c_i32, _c_i32, _c_i32]),
     "pa_decode": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32,

@@ -206,6 +206,26 @@ int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool
                                          n_new_tokens, static_cast<hipStream_t>(stream)));
 }
 
+int pa_rope_kv_append(pa_geom_t g, const void* q, void* q_out, const void* k_new,
+                      const void* v_new, void* k_pool, void* v_pool, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* cu_new_lens,
+                      const int32_t* ctx_lens, int32_t n_seqs, int32_t n_new_tokens,
+                      double rope_theta, const float* inv_freq, void* stream) {
+  int st = pa_geom_check(g);
+  if (st != PA_OK) return st;
+  if (n_new_tokens < 0 || n_seqs < 0 || max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if (!inv_freq && !(rope_theta > 0.0 && std::isfinite(rope_theta))) return PA_ERR_INVALID_ARG;
+  if ((q == nullptr) != (q_out == nullptr)) return PA_ERR_INVALID_ARG;
+  if (n_new_tokens == 0) return PA_OK;
+  if (n_seqs == 0) return PA_ERR_INVALID_ARG;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !cu_new_lens || !ctx_lens)
+    return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_rope_kv_append(
+      to_launch(g), q, q_out, k_new, v_new, k_pool, v_pool, block_tables, max_blocks_per_seq,
+      cu_new_lens, ctx_lens, n_seqs, n_new_tokens, rope_theta, inv_freq,
+      static_cast<hipStream_t>(stream)));
+}
+
 int32_t pa_decode_partition_tokens(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,
                                    int32_t partition_tokens) {
   const int st = decode_args_ok(g, n_seqs, max_ctx_len, partition_tokens);

@@ -23,6 +23,15 @@ hipError_t launch_kv_append(const LaunchGeom& geo, const void* k_new, const void
                             int max_blocks, const int32_t* cu_new_lens, const int32_t* ctx_lens,
                             int n_seqs, int n_new_tokens, hipStream_t stream);
 
+// Rotary position encoding of the new Q and K rows, K appended rotated and V as is.
+// inv_freq: head_dim/2 frequencies (device) or nullptr for rope_theta^(-2i/head_dim).
+hipError_t launch_rope_kv_append(const LaunchGeom& geo, const void* q_in, void* q_out,
+                                 const void* k_new, const void* v_new, void* k_pool,
+                                 void* v_pool, const int32_t* block_tables, int max_blocks,
+                                 const int32_t* cu_new_lens, const int32_t* ctx_lens,
+                                 int n_seqs, int n_new_tokens, double rope_theta,
+                                 const float* inv_freq, hipStream_t stream);
+
 // Decode: workgroups of four waves; every wave is one stream-K worker.
 constexpr int kDecodeWaves = 4;
 // A worker's range is at most this many tiles per KV head (so it touches at most this

@@ -237,3 +237,25 @@ def test_prefill_and_append_validation(lib):
     assert ap(max_blocks=0) == _lib.PA_ERR_INVALID_ARG
     assert ap(t=0, kn=None) == 0
     assert ap(g=geom(bs=64)) == _lib.PA_ERR_UNSUPPORTED
+
+
+def test_rope_append_validation(lib):
+    g = geom()
+    ra = lambda **k: lib.pa_rope_kv_append(k.get("g", g), k.get("q", FAKE), k.get("qo", FAKE),
+                                           k.get("kn", FAKE), FAKE, FAKE, FAKE, FAKE,
+                                           k.get("max_blocks", 4), FAKE, FAKE, k.get("n", 2),
+                                           k.get("t", 5), k.get("theta", 500000.0),
+                                           k.get("freq", None), None)
+    assert ra(kn=None) == _lib.PA_ERR_INVALID_ARG
+    assert ra(q=None) == _lib.PA_ERR_INVALID_ARG          # q without q_out or the reverse
+    assert ra(qo=None) == _lib.PA_ERR_INVALID_ARG
+    assert ra(t=-1) == _lib.PA_ERR_INVALID_ARG
+    assert ra(n=0) == _lib.PA_ERR_INVALID_ARG
+    assert ra(max_blocks=0) == _lib.PA_ERR_INVALID_ARG
+    for bad in (0.0, -2.0, float("inf"), float("nan")):
+        assert ra(theta=bad) == _lib.PA_ERR_INVALID_ARG
+    assert ra(t=0, theta=0.0, freq=FAKE) == 0             # a table replaces theta
+    assert ra(t=0, kn=None) == 0                          # nothing to do: no pointer read
+    assert ra(t=0) == 0
+    assert ra(g=geom(bs=64)) == _lib.PA_ERR_UNSUPPORTED
+    assert ra(g=geom(d=128)) == _lib.PA_ERR_UNSUPPORTED
