@@ -7,13 +7,18 @@ them on shared pages; block size 32; 32 query / 8 KV heads, head_dim 64, bf16). 
 the one workload that runs every step of the path (append, decode partitions, split-K
 merge, chunked prefill), so one step = one pass of the whole path.
 
-    python bench.py [--steps K] [--warmup W] [--workload mixed|decode-long|decode-batched|prefill]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload mixed|decode-long|decode-batched|prefill|rope-append]
 
 Prints one JSON line.  ``value`` = decode KV bytes read per step / wall time per step
 (whole step, all kernels).  ``roofline`` reports the dominant kernel (pa_decode, timed
 with HIP events on its stream) against HBM peak; ``roofline_prefill`` reports pa_prefill
 against dense bf16 MFMA peak.  ``cpu_baseline`` times the CPU oracle on a bounded sample
 of the same workload (layer 0) before the GPU is touched.
+
+``--workload rope-append`` times pa_rope_kv_append alone (RoPE of Q and K fused with the
+K/V append) on the 4608 new rows of the prefill workload, against HBM peak, with the
+plain pa_kv_append of the same rows beside it.
 """
 
 from __future__ import annotations
@@ -43,6 +48,7 @@ WORKLOADS = {
     "decode-long": 4,
     "decode-batched": 2,
     "prefill": 3,
+    "rope-append": 3,
 }
 
 
@@ -250,6 +256,66 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     return res
 
 
+def run_rope(cfg: int, steps: int, warmup: int) -> dict:
+    """pa_rope_kv_append over the new rows of workload ``cfg`` (one layer), timed with HIP
+    events per launch; pa_kv_append of the same rows timed the same way beside it."""
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    dev = torch.device("cuda:0")
+    case = W.make_case(cfg)
+    stream = torch.cuda.current_stream()
+
+    def up16(bits):
+        a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+        return torch.from_numpy(a).to(dev).view(torch.bfloat16)
+
+    geom = pa.Geometry(case.num_pages, case.block_size, case.num_q_heads, case.num_kv_heads,
+                       case.head_dim)
+    e = W.page_elems(case)
+    kp = torch.zeros((case.num_pages, e), dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    ctx = torch.from_numpy(case.ctx_lens).to(dev)
+    cu = torch.from_numpy(case.cu_new_lens).to(dev)
+    k_new, v_new = up16(case.k_new), up16(case.v_new)
+    t = int(case.k_new.shape[0])
+    q = up16(W.normal_bf16([77, cfg], t * case.num_q_heads * case.head_dim)).view(
+        t, case.num_q_heads, case.head_dim)
+    q_out = torch.empty_like(q)
+
+    def timed(fn, n):
+        ms = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ms.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([x.elapsed_time(y) for x, y in ms]))
+
+    rope = lambda: pa.rope_kv_append(geom, q, q_out, k_new, v_new, kp, vp, bt, cu, ctx,
+                                     rope_theta=500000.0, stream=stream)
+    plain = lambda: pa.kv_append(geom, k_new, v_new, kp, vp, bt, cu, ctx, stream=stream)
+    for _ in range(warmup):
+        rope()
+        plain()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    rope_ms = timed(rope, steps)
+    wall = time.perf_counter() - t0
+    plain_ms = timed(plain, steps)
+    row = case.num_kv_heads * case.head_dim * 2  # bytes of one token's K (or V) row
+    qrow = case.num_q_heads * case.head_dim * 2
+    nbytes = t * (2 * qrow + 4 * row)  # q read + written, K/V read + written
+    return {"rope_ms": rope_ms, "plain_ms": plain_ms, "bytes_per_launch": nbytes,
+            "plain_bytes_per_launch": t * 4 * row, "tokens": t, "ms_per_step": wall * 1e3 / steps,
+            "gbps": nbytes / (rope_ms * 1e-3) / 1e9,
+            "plain_gbps": t * 4 * row / (plain_ms * 1e-3) / 1e9}
+
+
 def copy_calibration(nbytes: int, reps: int) -> dict:
     """Device-to-device copy of ``nbytes`` (torch's copy kernel), timed with HIP events.
 
@@ -303,6 +369,8 @@ def main() -> int:
         print(json.dumps(copy_calibration(args.copy_bytes, max(2, args.steps))), flush=True)
         return 0
     cfg = WORKLOADS[args.workload]
+    if args.workload == "rope-append":
+        return main_rope(args, cfg)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -356,6 +424,74 @@ def main() -> int:
                      "avg_launch_ms": round(res["prefill_ms"], 5)}
     line["append_ms_per_layer"] = round(res["append_ms"], 5)
     line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline_rope(cfg: int, budget_s: float) -> dict:
+    """The RoPE oracle (fp64 rotation + append) on a bounded prefix of the same rows."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    case = W.make_case(cfg)
+    t = int(case.k_new.shape[0])
+    q = W.normal_bf16([77, cfg], t * case.num_q_heads * case.head_dim).reshape(
+        t, case.num_q_heads, case.head_dim)
+    kp, vp = W.sentinel_pool(case), W.sentinel_pool(case)
+    f = O.rope_freqs(case.head_dim, 500000.0)
+    row = case.num_kv_heads * case.head_dim * 2
+    qrow = case.num_q_heads * case.head_dim * 2
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        for s in range(case.n_seqs):
+            a, b = int(case.cu_new_lens[s]), int(case.cu_new_lens[s + 1])
+            O.rope_kv_append(q[a:b], case.k_new[a:b], case.v_new[a:b], kp, vp,
+                             case.block_tables[s:s + 1], np.array([0, b - a]),
+                             case.ctx_lens[s:s + 1], case.block_size, f)
+            done += b - a
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": done * (2 * qrow + 4 * row) / dt / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 numpy RoPE + append oracle on {done} of {t} rows in {dt:.1f} s, "
+                      f"1 thread"}
+
+
+def main_rope(args, cfg: int) -> int:
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline_rope(cfg, args.cpu_budget)
+    res = run_rope(cfg, args.steps, args.warmup)
+    base = W.make_case(cfg, values=False)
+    line = {
+        "metric": METRIC,
+        "value": round(res["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled pages)",
+        "config": {"workload": f"rope-append-{res['tokens']}tokens-bs{base.block_size}",
+                   "layers": 1, "block_size": base.block_size, "num_q_heads": 32,
+                   "num_kv_heads": 8, "head_dim": 64, "rope_theta": 500000.0},
+        "roofline": {"bound": "hbm", "kernel": "pa_rope_kv_append (append_kernel<bs, rope>)",
+                     "achieved": round(res["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(res["gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": hbm_traffic("rope-append"),
+                     "bytes_per_launch": res["bytes_per_launch"],
+                     "avg_launch_ms": round(res["rope_ms"], 5)},
+        "plain_append": {"kernel": "pa_kv_append", "bytes_per_launch": res["plain_bytes_per_launch"],
+                         "avg_launch_ms": round(res["plain_ms"], 5),
+                         "achieved_gbps": round(res["plain_gbps"], 1)},
+        "cpu_baseline": cpu,
+    }
     print(json.dumps(line), flush=True)
     return 0
 
