@@ -19,3 +19,4 @@ from .paged_attention import (  # noqa: F401
     v_offset,
 )
 from .rope import f64_to_bf16, positions, rope_freqs, rope_kv_append, rotate  # noqa: F401,E402
+from .pages import copy_pages, cow_needs  # noqa: F401,E402
