@@ -117,6 +117,16 @@ int pa_pool_share(pa_pool_t* p, int32_t n, const int32_t* ids);
  * already free, counting repeats within `ids`. */
 int pa_pool_free(pa_pool_t* p, int32_t n, const int32_t* ids);
 
+/* Copy-on-write decision ([guide] §PagedAttention: shared pages make copy-on-write
+ * straightforward).  `ids` are the pages a caller is about to write (its block-table
+ * entries), taken in order: an entry whose page has more than one reference at its turn
+ * drops one reference and receives a fresh page (reference count 1) in ids_out[i]; an
+ * entry whose page has a single reference keeps it (ids_out[i] = ids[i]).  The caller then
+ * copies every changed pair with pa_copy_pages and points its block table at ids_out.
+ * All or nothing: PA_ERR_OUT_OF_PAGES (not enough free pages for the copies) or
+ * PA_ERR_INVALID_ARG (an id out of range or free) leaves the pool unchanged. */
+int pa_pool_cow(pa_pool_t* p, int32_t n, const int32_t* ids, int32_t* ids_out);
+
 /* Pages currently on the free list (-1 for a NULL pool). */
 int32_t pa_pool_num_free(const pa_pool_t* p);
 
@@ -141,6 +151,18 @@ int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool
                  void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
                  const int32_t* cu_new_lens, const int32_t* ctx_lens, int32_t n_seqs,
                  int32_t n_new_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * copy_pages (the copy half of copy-on-write, [guide] §PagedAttention).  Copies whole
+ * page src_pages[i] onto page dst_pages[i] in both pools (every KV head, every slot), bit
+ * for bit, for i < n.
+ *   src_pages, dst_pages  int32 [n] (device)
+ * Pairs with an id outside [0, num_pages) or with src == dst are skipped.  The
+ * destination pages must be distinct and none of them a source (the pairs run in no
+ * particular order).  n == 0 is a no-op.
+ * ------------------------------------------------------------------------------- */
+int pa_copy_pages(pa_geom_t g, void* k_pool, void* v_pool, const int32_t* src_pages,
+                  const int32_t* dst_pages, int32_t n, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * rope_kv_append ([guide] §Llama 3.2 1B架构拆解: rotary position encoding turns Q and K

@@ -22,6 +22,7 @@ from . import _lib
 
 __all__ = [
     "PagedAttnError", "Geometry", "PagePool", "page_bytes", "kv_append", "rope_kv_append",
+    "copy_pages",
     "decode_partition_tokens", "decode_workspace_bytes", "decode", "prefill_workspace_bytes",
     "prefill", "library",
 ]
@@ -107,6 +108,13 @@ class PagePool:
     def free(self, ids: Sequence[int]) -> None:
         _check(self._lib.pa_pool_free(self._h, len(ids), self._ids(ids)), "pa_pool_free")
 
+    def cow(self, ids: Sequence[int]) -> list[int]:
+        """Copy-on-write decision for pages about to be written (see pa_pool_cow): the
+        page each entry should write, a fresh one where the original is shared."""
+        out = (ctypes.c_int32 * max(1, len(ids)))()
+        _check(self._lib.pa_pool_cow(self._h, len(ids), self._ids(ids), out), "pa_pool_cow")
+        return list(out[:len(ids)])
+
     def num_free(self) -> int:
         return int(self._lib.pa_pool_num_free(self._h))
 
@@ -166,6 +174,21 @@ def kv_append(geom: Geometry, k_new, v_new, k_pool, v_pool, block_tables, cu_new
                                   _ptr(block_tables), int(block_tables.shape[1]),
                                   _ptr(cu_new_lens), _ptr(ctx_lens), n_seqs, t, _stream(stream))
     _check(st, "pa_kv_append")
+
+
+def copy_pages(geom: Geometry, k_pool, v_pool, src_pages, dst_pages, stream=None) -> None:
+    """Copy whole pages src_pages[i] -> dst_pages[i] (int32 device tensors) in both pools
+    (see pa_copy_pages)."""
+    import torch
+
+    n = int(src_pages.numel())
+    for name, x in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(x, name, torch.bfloat16, geom.num_pages * geom.page_elems)
+    _dev(src_pages, "src_pages", torch.int32, n)
+    _dev(dst_pages, "dst_pages", torch.int32, n)
+    st = _lib.load().pa_copy_pages(geom.c(), _ptr(k_pool), _ptr(v_pool), _ptr(src_pages),
+                                   _ptr(dst_pages), n, _stream(stream))
+    _check(st, "pa_copy_pages")
 
 
 def rope_kv_append(geom: Geometry, q, q_out, k_new, v_new, k_pool, v_pool, block_tables,

@@ -42,10 +42,12 @@ SIGNATURES = {
     "pa_pool_alloc": (ctypes.c_int, [_c_p, _c_i32, _c_i32p]),
     "pa_pool_share": (ctypes.c_int, [_c_p, _c_i32, _c_i32p]),
     "pa_pool_free": (ctypes.c_int, [_c_p, _c_i32, _c_i32p]),
+    "pa_pool_cow": (ctypes.c_int, [_c_p, _c_i32, _c_i32p, _c_i32p]),
     "pa_pool_num_free": (_c_i32, [_c_p]),
     "pa_pool_refcount": (_c_i32, [_c_p, _c_i32]),
     "pa_kv_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p,
                                     _c_i32, _c_i32, _c_p]),
+    "pa_copy_pages": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p]),
     "pa_rope_kv_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                          _c_i32, _c_p, _c_p, _c_i32, _c_i32, ctypes.c_double,
                                          _c_p, _c_p]),

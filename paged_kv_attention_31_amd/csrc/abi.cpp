@@ -173,6 +173,46 @@ int pa_pool_free(pa_pool_t* p, int32_t n, const int32_t* ids) {
   return PA_OK;
 }
 
+int pa_pool_cow(pa_pool_t* p, int32_t n, const int32_t* ids, int32_t* ids_out) {
+  if (!p || n < 0 || (n > 0 && (!ids || !ids_out))) return PA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(p->mu);
+  const int32_t np = (int32_t)p->refs.size();
+  // validate and count the copies first (entry by entry), so a failing call changes nothing
+  size_t copies = 0;
+  {
+    std::vector<int32_t> seen_ids;
+    std::vector<int32_t> seen_refs;
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t id = ids[i];
+      if (id < 0 || id >= np || p->refs[id] <= 0) return PA_ERR_INVALID_ARG;
+      size_t k = 0;
+      while (k < seen_ids.size() && seen_ids[k] != id) ++k;
+      if (k == seen_ids.size()) {
+        seen_ids.push_back(id);
+        seen_refs.push_back(p->refs[id]);
+      }
+      if (seen_refs[k] > 1) {
+        --seen_refs[k];
+        ++copies;
+      }
+    }
+  }
+  if (copies > p->free_list.size()) return PA_ERR_OUT_OF_PAGES;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    if (p->refs[id] > 1) {
+      --p->refs[id];
+      const int32_t fresh = p->free_list.back();
+      p->free_list.pop_back();
+      p->refs[fresh] = 1;
+      ids_out[i] = fresh;
+    } else {
+      ids_out[i] = id;
+    }
+  }
+  return PA_OK;
+}
+
 int32_t pa_pool_num_free(const pa_pool_t* p) {
   if (!p) return -1;
   std::lock_guard<std::mutex> lock(const_cast<pa_pool*>(p)->mu);
@@ -224,6 +264,17 @@ int pa_rope_kv_append(pa_geom_t g, const void* q, void* q_out, const void* k_new
       to_launch(g), q, q_out, k_new, v_new, k_pool, v_pool, block_tables, max_blocks_per_seq,
       cu_new_lens, ctx_lens, n_seqs, n_new_tokens, rope_theta, inv_freq,
       static_cast<hipStream_t>(stream)));
+}
+
+int pa_copy_pages(pa_geom_t g, void* k_pool, void* v_pool, const int32_t* src_pages,
+                  const int32_t* dst_pages, int32_t n, void* stream) {
+  int st = pa_geom_check(g);
+  if (st != PA_OK) return st;
+  if (n < 0) return PA_ERR_INVALID_ARG;
+  if (n == 0) return PA_OK;
+  if (!k_pool || !v_pool || !src_pages || !dst_pages) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_copy_pages(to_launch(g), k_pool, v_pool, src_pages, dst_pages, n,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int32_t pa_decode_partition_tokens(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,

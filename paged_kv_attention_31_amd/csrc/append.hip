@@ -334,7 +334,49 @@ hipError_t launch_append(const LaunchGeom& geo, const void* q_in, void* q_out, c
   return hipGetLastError();
 }
 
+// Copy-on-write: one workgroup per (src, dst) page pair copies the whole page of both
+// pools with 16-byte loads and stores; a pair with an id outside the pool is skipped.
+__global__ __launch_bounds__(256) void copy_pages_kernel(
+    uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+    const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int num_pages,
+    int page_chunks) {
+  const int s = src[blockIdx.x], d = dst[blockIdx.x];
+  if ((unsigned)s >= (unsigned)num_pages || (unsigned)d >= (unsigned)num_pages || s == d) return;
+  const size_t so = (size_t)s * page_chunks, dof = (size_t)d * page_chunks;
+  auto* k = reinterpret_cast<u32x4_t*>(k_pool);
+  auto* v = reinterpret_cast<u32x4_t*>(v_pool);
+  for (int c = threadIdx.x; c < page_chunks; c += 1024) {
+    u32x4_t a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = c + 256 * i;
+      if (ci < page_chunks) {
+        a[i] = k[so + ci];
+        b[i] = v[so + ci];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ci = c + 256 * i;
+      if (ci < page_chunks) {
+        k[dof + ci] = a[i];
+        v[dof + ci] = b[i];
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_pages(const LaunchGeom& geo, void* k_pool, void* v_pool,
+                             const int32_t* src_pages, const int32_t* dst_pages, int n,
+                             hipStream_t stream) {
+  const int page_chunks = geo.block_size * geo.num_kv_heads * kHeadDim / 8;  // 16-byte chunks
+  hipLaunchKernelGGL(copy_pages_kernel, dim3(n), dim3(256), 0, stream,
+                     static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), src_pages,
+                     dst_pages, geo.num_pages, page_chunks);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const LaunchGeom& geo, const void* k_new, const void* v_new,
                             void* k_pool, void* v_pool, const int32_t* block_tables,

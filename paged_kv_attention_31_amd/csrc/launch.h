@@ -32,6 +32,11 @@ hipError_t launch_rope_kv_append(const LaunchGeom& geo, const void* q_in, void* 
                                  int n_seqs, int n_new_tokens, double rope_theta,
                                  const float* inv_freq, hipStream_t stream);
 
+// Copy whole pages src_pages[i] -> dst_pages[i] (device id arrays) in both pools.
+hipError_t launch_copy_pages(const LaunchGeom& geo, void* k_pool, void* v_pool,
+                             const int32_t* src_pages, const int32_t* dst_pages, int n,
+                             hipStream_t stream);
+
 // Decode: workgroups of four waves; every wave is one stream-K worker.
 constexpr int kDecodeWaves = 4;
 // A worker's range is at most this many tiles per KV head (so it touches at most this

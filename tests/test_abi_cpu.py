@@ -259,3 +259,63 @@ def test_rope_append_validation(lib):
     assert ra(t=0) == 0
     assert ra(g=geom(bs=64)) == _lib.PA_ERR_UNSUPPORTED
     assert ra(g=geom(d=128)) == _lib.PA_ERR_UNSUPPORTED
+
+
+def test_pool_cow_matches_the_oracle_decisions():
+    import numpy as np
+
+    import oracle as O
+    from paged_kv_attention_31_amd import PagePool
+
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        pool = PagePool(64)
+        pages = pool.alloc(int(rng.integers(4, 20)))
+        refs = {p: 1 for p in pages}
+        for p in rng.choice(pages, size=int(rng.integers(0, 30))).tolist():
+            pool.share([p])
+            refs[p] += 1
+        ids = rng.choice(pages, size=int(rng.integers(1, 12))).tolist()
+        free_before = pool.num_free()
+        need, refs_after = O.cow_needs(refs, ids)
+        if sum(need) > free_before:
+            with pytest.raises(Exception):
+                pool.cow(ids)
+            assert pool.num_free() == free_before
+            assert all(pool.refcount(p) == refs[p] for p in pages)
+            continue
+        out = pool.cow(ids)
+        fresh = [o for o, n in zip(out, need) if n]
+        assert [o == i for o, i in zip(out, ids)] == [not n for n in need]
+        assert len(set(fresh)) == len(fresh) and not set(fresh) & set(pages)
+        assert all(pool.refcount(f) == 1 for f in fresh)
+        assert all(pool.refcount(p) == refs_after[p] for p in pages)
+        assert pool.num_free() == free_before - len(fresh)
+
+
+def test_pool_cow_all_or_nothing(lib):
+    from paged_kv_attention_31_amd import PagePool
+
+    pool = PagePool(3)
+    a, b, c = pool.alloc(3)
+    pool.share([a, b])
+    with pytest.raises(Exception):
+        pool.cow([a, b])           # two copies needed, no free page
+    assert pool.refcount(a) == 2 and pool.refcount(b) == 2 and pool.num_free() == 0
+    with pytest.raises(Exception):
+        pool.cow([a, 99])          # bad id: nothing changes
+    assert pool.refcount(a) == 2
+    pool.free([c])
+    out = pool.cow([a])
+    assert out == [c] and pool.refcount(a) == 1 and pool.refcount(c) == 1
+
+
+def test_copy_pages_validation(lib):
+    g = geom()
+    cp = lambda **k: lib.pa_copy_pages(k.get("g", g), k.get("kp", FAKE), FAKE, k.get("src", FAKE),
+                                       FAKE, k.get("n", 3), None)
+    assert cp(kp=None) == _lib.PA_ERR_INVALID_ARG
+    assert cp(src=None) == _lib.PA_ERR_INVALID_ARG
+    assert cp(n=-1) == _lib.PA_ERR_INVALID_ARG
+    assert cp(n=0, kp=None) == 0
+    assert cp(g=geom(bs=8)) == _lib.PA_ERR_UNSUPPORTED
