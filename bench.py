@@ -8,7 +8,7 @@ the one workload that runs every step of the path (append, decode partitions, sp
 merge, chunked prefill), so one step = one pass of the whole path.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload mixed|decode-long|decode-batched|prefill|rope-append]
+                    [--workload mixed|decode-long|decode-batched|prefill|rope-append|copy-pages]
 
 Prints one JSON line.  ``value`` = decode KV bytes read per step / wall time per step
 (whole step, all kernels).  ``roofline`` reports the dominant kernel (pa_decode, timed
@@ -18,7 +18,8 @@ of the same workload (layer 0) before the GPU is touched.
 
 ``--workload rope-append`` times pa_rope_kv_append alone (RoPE of Q and K fused with the
 K/V append) on the 4608 new rows of the prefill workload, against HBM peak, with the
-plain pa_kv_append of the same rows beside it.
+plain pa_kv_append of the same rows beside it.  ``--workload copy-pages`` times
+pa_copy_pages (the copy half of copy-on-write) on 4096 block-size-32 pages of both pools.
 """
 
 from __future__ import annotations
@@ -49,7 +50,9 @@ WORKLOADS = {
     "decode-batched": 2,
     "prefill": 3,
     "rope-append": 3,
+    "copy-pages": 0,
 }
+COPY_PAGES, COPY_BS = 4096, 32
 
 
 def log(msg: str) -> None:
@@ -371,6 +374,8 @@ def main() -> int:
     cfg = WORKLOADS[args.workload]
     if args.workload == "rope-append":
         return main_rope(args, cfg)
+    if args.workload == "copy-pages":
+        return main_copy(args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -424,6 +429,83 @@ def main() -> int:
                      "avg_launch_ms": round(res["prefill_ms"], 5)}
     line["append_ms_per_layer"] = round(res["append_ms"], 5)
     line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_copy(steps: int, warmup: int) -> dict:
+    """pa_copy_pages of COPY_PAGES pages onto as many others, both pools, HIP-event timed."""
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    dev = torch.device("cuda:0")
+    n_pages = 2 * COPY_PAGES
+    e = COPY_BS * 8 * 64
+    kp = torch.empty((n_pages, e), dtype=torch.bfloat16, device=dev).normal_()
+    vp = torch.empty_like(kp).normal_()
+    perm = np.random.default_rng(7).permutation(n_pages).astype(np.int32)
+    src = torch.from_numpy(perm[:COPY_PAGES].copy()).to(dev)
+    dst = torch.from_numpy(perm[COPY_PAGES:].copy()).to(dev)
+    geom = pa.Geometry(n_pages, COPY_BS, 32, 8, 64)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        pa.copy_pages(geom, kp, vp, src, dst, stream=stream)
+    torch.cuda.synchronize()
+    ev = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        pa.copy_pages(geom, kp, vp, src, dst, stream=stream)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    nbytes = COPY_PAGES * e * 2 * 2 * 2  # both pools, read + written
+    return {"ms": ms, "bytes_per_launch": nbytes, "gbps": nbytes / (ms * 1e-3) / 1e9,
+            "ms_per_step": wall * 1e3 / steps}
+
+
+def cpu_baseline_copy(budget_s: float) -> dict:
+    """The oracle's page copies (numpy) on a bounded sample of the same pairs."""
+    import oracle as O
+
+    e = COPY_BS * 8 * 64
+    n = 512  # pages per pool in the sample (the oracle holds both pools in host memory)
+    kp = np.random.default_rng(1).integers(0, 1 << 16, (2 * n, e), dtype=np.uint16)
+    vp = kp.copy()
+    perm = np.random.default_rng(7).permutation(2 * n)
+    t0, reps = time.perf_counter(), 0
+    while time.perf_counter() - t0 < min(budget_s, 5.0) or reps == 0:
+        O.copy_pages(kp, vp, perm[:n], perm[n:])
+        reps += 1
+    dt = time.perf_counter() - t0
+    return {"value": reps * n * e * 2 * 2 * 2 / dt / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"numpy oracle copy of {n} block-size-32 page pairs x {reps} in {dt:.1f} s, "
+                      f"1 thread"}
+
+
+def main_copy(args) -> int:
+    cpu = None if args.no_cpu_baseline else cpu_baseline_copy(args.cpu_budget)
+    res = run_copy(args.steps, args.warmup)
+    line = {
+        "metric": METRIC, "value": round(res["gbps"], 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) bf16 pools, seeded page permutation)",
+        "config": {"workload": f"copy-pages-{COPY_PAGES}x-bs{COPY_BS}", "layers": 1,
+                   "block_size": COPY_BS, "num_kv_heads": 8, "head_dim": 64},
+        "roofline": {"bound": "hbm", "kernel": "pa_copy_pages (copy_pages_kernel)",
+                     "achieved": round(res["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(res["gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": hbm_traffic("copy-pages"),
+                     "bytes_per_launch": res["bytes_per_launch"],
+                     "avg_launch_ms": round(res["ms"], 5)},
+        "cpu_baseline": cpu,
+    }
     print(json.dumps(line), flush=True)
     return 0
 
