@@ -11,7 +11,8 @@ merge, chunked prefill), so one step = one pass of the whole path.
                     [--workload mixed|decode-long|decode-batched|prefill|rope-append|copy-pages]
 
 Prints one JSON line.  ``value`` = decode KV bytes read per step / wall time per step
-(whole step, all kernels).  ``roofline`` reports the dominant kernel (pa_decode, timed
+(whole step, all kernels), the step captured once in a HIP graph and replayed (the eager
+step time is reported beside it).  ``roofline`` reports the dominant kernel (pa_decode, timed
 with HIP events on its stream) against HBM peak; ``roofline_prefill`` reports pa_prefill
 against dense bf16 MFMA peak.  ``cpu_baseline`` times the CPU oracle on a bounded sample
 of the same workload (layer 0) before the GPU is touched.
@@ -192,13 +193,12 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
                           device=dev)
     stream = torch.cuda.current_stream()
     scale = base.scale
-    n_new = int(base.new_lens.sum())
 
     ev_dec = [] if n_dec else None
     ev_pre = [] if n_pre else None
     ev_app = []
 
-    def step(record: bool):
+    def step(record: bool, stream):
         for L in layers:
             if record:
                 a0 = torch.cuda.Event(enable_timing=True)
@@ -226,12 +226,30 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
                     ev_dec.append((d0, e))
 
     for _ in range(warmup):
-        step(False)
+        step(False, stream)
     torch.cuda.synchronize()
-    log(f"timing {steps} steps")
+    # per-kernel times: eager steps with HIP events around every launch
+    log(f"timing {steps} eager steps (per-kernel events)")
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(True)
+        step(True, stream)
+    torch.cuda.synchronize()
+    wall_eager = time.perf_counter() - t0
+    # whole-step time: the same step captured once in a HIP graph and replayed, which
+    # removes the host launch gaps between the 16 x 3 launches
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=cap):
+        step(False, cap)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    log(f"timing {steps} graph replays")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
@@ -239,8 +257,8 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
         return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
 
     ms_step = wall * 1e3 / steps
-    res = {"ms_per_step": ms_step, "n_layers": n_layers, "partition_tokens": part,
-           "append_ms": avg_ms(ev_app)}
+    res = {"ms_per_step": ms_step, "ms_per_step_eager": wall_eager * 1e3 / steps,
+           "n_layers": n_layers, "partition_tokens": part, "append_ms": avg_ms(ev_app)}
     kv_bytes_layer = base.kv_tokens() * KV_BYTES_PER_TOKEN
     if n_dec:
         dec_ms = avg_ms(ev_dec)
@@ -406,6 +424,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 K/V/Q, shuffled pages)",
         "config": config,
+        "step_timing": {"graph_replay_ms": round(res["ms_per_step"], 4),
+                        "eager_ms": round(res["ms_per_step_eager"], 4)},
     }
     if "decode_ms" in res:
         ach = res["decode_gbps"]
