@@ -20,3 +20,4 @@ from .paged_attention import (  # noqa: F401
 )
 from .rope import f64_to_bf16, positions, rope_freqs, rope_kv_append, rotate  # noqa: F401,E402
 from .pages import copy_pages, cow_needs  # noqa: F401,E402
+from .norm import residual_rmsnorm, silu_mul  # noqa: F401,E402
