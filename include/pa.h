@@ -165,6 +165,37 @@ int pa_copy_pages(pa_geom_t g, void* k_pool, void* v_pool, const int32_t* src_pa
                   const int32_t* dst_pages, int32_t n, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * residual_rmsnorm ([guide] §Llama 3.2 1B架构拆解: RMS normalisation and a residual
+ * connection around every sub-layer; [实战] §算子融合: the residual add fused into the
+ * normalisation).  Per row of `hidden` values:
+ *   h = x + residual_in (rounded to bf16 and stored in residual_out, the next residual),
+ *   out = h / sqrt(mean(h^2) + eps) * gamma, rounded once to bf16 (nearest even).
+ * Sums and products run in fp32.
+ *   x, out                  [n_rows][hidden] bf16 (device)
+ *   residual_in, residual_out  [n_rows][hidden] bf16 (device); residual_out may be
+ *                           residual_in (in place); both NULL for h = x
+ *   gamma                   [hidden] bf16 (device)
+ *   hidden                  a multiple of 8, at most 8192 (else PA_ERR_UNSUPPORTED)
+ *   eps                     >= 0, finite (1e-5 for the Llama 3 family)
+ * PA_ERR_INVALID_ARG for a missing pointer, exactly one residual pointer, or bad sizes.
+ * ------------------------------------------------------------------------------- */
+int pa_residual_rmsnorm(const void* x, const void* residual_in, void* residual_out,
+                        const void* gamma, void* out, int32_t n_rows, int32_t hidden, float eps,
+                        void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * silu_mul ([guide] §Llama 3.2 1B架构拆解: SiLU of the gate projection times the up
+ * projection, element-wise).  out[t][j] = g / (1 + e^-g) * u with g = gate[t*ld_in + j],
+ * u = up[t*ld_in + j], in fp32, rounded once to bf16; written to out[t*ld_out + j], for
+ * j < width.  A concatenated [n_rows][2*width] gate|up buffer is gate = base,
+ * up = base + width, ld_in = 2*width.
+ *   width, ld_in, ld_out    multiples of 8 with ld_in, ld_out >= width (elements)
+ * PA_ERR_INVALID_ARG for a missing pointer or bad sizes.
+ * ------------------------------------------------------------------------------- */
+int pa_silu_mul(const void* gate, const void* up, int64_t ld_in, void* out, int64_t ld_out,
+                int32_t n_rows, int32_t width, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * rope_kv_append ([guide] §Llama 3.2 1B架构拆解: rotary position encoding turns Q and K
  * by the token's position before attention; §推理流程：从Prefill到Decode: K/V join the
  * cache before the token attends).  For the same rows, positions and pages as

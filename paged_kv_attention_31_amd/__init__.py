@@ -22,7 +22,7 @@ from . import _lib
 
 __all__ = [
     "PagedAttnError", "Geometry", "PagePool", "page_bytes", "kv_append", "rope_kv_append",
-    "copy_pages",
+    "copy_pages", "residual_rmsnorm", "silu_mul",
     "decode_partition_tokens", "decode_workspace_bytes", "decode", "prefill_workspace_bytes",
     "prefill", "library",
 ]
@@ -189,6 +189,46 @@ def copy_pages(geom: Geometry, k_pool, v_pool, src_pages, dst_pages, stream=None
     st = _lib.load().pa_copy_pages(geom.c(), _ptr(k_pool), _ptr(v_pool), _ptr(src_pages),
                                    _ptr(dst_pages), n, _stream(stream))
     _check(st, "pa_copy_pages")
+
+
+def residual_rmsnorm(x, gamma, out, residual_in=None, residual_out=None, eps: float = 1e-5,
+                     stream=None) -> None:
+    """out = RMSNorm(x + residual_in) * gamma per row; the sum goes to residual_out (see
+    pa_residual_rmsnorm).  Tensors are bf16 [rows, hidden] (gamma [hidden])."""
+    import torch
+
+    _need(x.dim() == 2, "x must be [rows, hidden]")
+    rows, hidden = int(x.shape[0]), int(x.shape[1])
+    for name, t in (("x", x), ("out", out)):
+        _dev(t, name, torch.bfloat16, rows * hidden)
+    _dev(gamma, "gamma", torch.bfloat16, hidden)
+    _need((residual_in is None) == (residual_out is None),
+          "residual_in and residual_out must both be given or both be None")
+    if residual_in is not None:
+        for name, t in (("residual_in", residual_in), ("residual_out", residual_out)):
+            _dev(t, name, torch.bfloat16, rows * hidden)
+    st = _lib.load().pa_residual_rmsnorm(_ptr(x), _ptr(residual_in), _ptr(residual_out),
+                                         _ptr(gamma), _ptr(out), rows, hidden, float(eps),
+                                         _stream(stream))
+    _check(st, "pa_residual_rmsnorm")
+
+
+def silu_mul(gate, up, out, stream=None) -> None:
+    """out = silu(gate) * up (see pa_silu_mul).  gate / up / out are bf16 [rows, width]
+    views with unit stride along width and equal row strides for gate and up (a
+    concatenated gate|up buffer's two halves qualify)."""
+    import torch
+
+    _need(gate.dim() == 2 and up.dim() == 2 and out.dim() == 2, "2-d views expected")
+    rows, width = int(gate.shape[0]), int(gate.shape[1])
+    _need(tuple(up.shape) == (rows, width) and tuple(out.shape) == (rows, width), "shapes differ")
+    for name, t in (("gate", gate), ("up", up), ("out", out)):
+        _need(t.is_cuda and t.dtype == torch.bfloat16 and t.stride(1) == 1,
+              f"{name} must be a bf16 device view with unit inner stride")
+    _need(gate.stride(0) == up.stride(0), "gate and up need the same row stride")
+    st = _lib.load().pa_silu_mul(_ptr(gate), _ptr(up), int(gate.stride(0)), _ptr(out),
+                                 int(out.stride(0)), rows, width, _stream(stream))
+    _check(st, "pa_silu_mul")
 
 
 def rope_kv_append(geom: Geometry, q, q_out, k_new, v_new, k_pool, v_pool, block_tables,

@@ -48,6 +48,10 @@ SIGNATURES = {
     "pa_kv_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p,
                                     _c_i32, _c_i32, _c_p]),
     "pa_copy_pages": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p]),
+    "pa_residual_rmsnorm": (ctypes.c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                           ctypes.c_float, _c_p]),
+    "pa_silu_mul": (ctypes.c_int, [_c_p, _c_p, ctypes.c_int64, _c_p, ctypes.c_int64, _c_i32,
+                                   _c_i32, _c_p]),
     "pa_rope_kv_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                          _c_i32, _c_p, _c_p, _c_i32, _c_i32, ctypes.c_double,
                                          _c_p, _c_p]),

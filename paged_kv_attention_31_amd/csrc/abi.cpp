@@ -277,6 +277,30 @@ int pa_copy_pages(pa_geom_t g, void* k_pool, void* v_pool, const int32_t* src_pa
                                           static_cast<hipStream_t>(stream)));
 }
 
+int pa_residual_rmsnorm(const void* x, const void* residual_in, void* residual_out,
+                        const void* gamma, void* out, int32_t n_rows, int32_t hidden, float eps,
+                        void* stream) {
+  if (n_rows < 0 || hidden <= 0 || hidden % 8 != 0 || !(eps >= 0.f) || !std::isfinite(eps))
+    return PA_ERR_INVALID_ARG;
+  if (hidden > pa::rmsnorm_max_hidden()) return PA_ERR_UNSUPPORTED;
+  if ((residual_in == nullptr) != (residual_out == nullptr)) return PA_ERR_INVALID_ARG;
+  if (n_rows == 0) return PA_OK;
+  if (!x || !gamma || !out) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_residual_rmsnorm(x, residual_in, residual_out, gamma, out, n_rows,
+                                                hidden, eps, static_cast<hipStream_t>(stream)));
+}
+
+int pa_silu_mul(const void* gate, const void* up, int64_t ld_in, void* out, int64_t ld_out,
+                int32_t n_rows, int32_t width, void* stream) {
+  if (n_rows < 0 || width <= 0 || width % 8 != 0) return PA_ERR_INVALID_ARG;
+  if (ld_in < width || ld_out < width || ld_in % 8 != 0 || ld_out % 8 != 0)
+    return PA_ERR_INVALID_ARG;
+  if (n_rows == 0) return PA_OK;
+  if (!gate || !up || !out) return PA_ERR_INVALID_ARG;
+  return hip_status(pa::launch_silu_mul(gate, up, ld_in, out, ld_out, n_rows, width,
+                                        compute_units(), static_cast<hipStream_t>(stream)));
+}
+
 int32_t pa_decode_partition_tokens(pa_geom_t g, int32_t n_seqs, int32_t max_ctx_len,
                                    int32_t partition_tokens) {
   const int st = decode_args_ok(g, n_seqs, max_ctx_len, partition_tokens);

@@ -37,6 +37,15 @@ hipError_t launch_copy_pages(const LaunchGeom& geo, void* k_pool, void* v_pool,
                              const int32_t* src_pages, const int32_t* dst_pages, int n,
                              hipStream_t stream);
 
+// Residual add + RMS normalisation of bf16 rows, and the SiLU-gated product.
+int rmsnorm_max_hidden();
+hipError_t launch_residual_rmsnorm(const void* x, const void* residual_in, void* residual_out,
+                                   const void* gamma, void* out, int n_rows, int hidden,
+                                   float eps, hipStream_t stream);
+hipError_t launch_silu_mul(const void* gate, const void* up, int64_t ld_in, void* out,
+                           int64_t ld_out, int n_rows, int width, int compute_units,
+                           hipStream_t stream);
+
 // Decode: workgroups of four waves; every wave is one stream-K worker.
 constexpr int kDecodeWaves = 4;
 // A worker's range is at most this many tiles per KV head (so it touches at most this

@@ -319,3 +319,25 @@ def test_copy_pages_validation(lib):
     assert cp(n=-1) == _lib.PA_ERR_INVALID_ARG
     assert cp(n=0, kp=None) == 0
     assert cp(g=geom(bs=8)) == _lib.PA_ERR_UNSUPPORTED
+
+
+def test_norm_and_silu_validation(lib):
+    rn = lambda **k: lib.pa_residual_rmsnorm(k.get("x", FAKE), k.get("ri", None), k.get("ro", None),
+                                             k.get("gm", FAKE), FAKE, k.get("n", 4),
+                                             k.get("h", 2048), k.get("eps", 1e-5), None)
+    assert rn(x=None) == _lib.PA_ERR_INVALID_ARG
+    assert rn(ri=FAKE) == _lib.PA_ERR_INVALID_ARG            # residual in without out
+    assert rn(h=2044) == _lib.PA_ERR_INVALID_ARG             # not a multiple of 8
+    assert rn(h=0) == _lib.PA_ERR_INVALID_ARG
+    assert rn(h=8200) == _lib.PA_ERR_UNSUPPORTED
+    assert rn(eps=-1.0) == _lib.PA_ERR_INVALID_ARG
+    assert rn(eps=float("nan")) == _lib.PA_ERR_INVALID_ARG
+    assert rn(n=-1) == _lib.PA_ERR_INVALID_ARG
+    assert rn(n=0, x=None) == 0
+    sm = lambda **k: lib.pa_silu_mul(k.get("g", FAKE), FAKE, k.get("ldi", 8192), FAKE,
+                                     k.get("ldo", 8192), k.get("n", 4), k.get("w", 8192), None)
+    assert sm(g=None) == _lib.PA_ERR_INVALID_ARG
+    assert sm(w=12) == _lib.PA_ERR_INVALID_ARG
+    assert sm(ldi=8184) == _lib.PA_ERR_INVALID_ARG           # row stride below the width
+    assert sm(ldo=8196) == _lib.PA_ERR_INVALID_ARG           # not 16-byte aligned rows
+    assert sm(n=0, g=None) == 0

@@ -1,0 +1,77 @@
+"""Parity of pa_residual_rmsnorm and pa_silu_mul against the CPU oracle (marked ``gpu``).
+
+Tolerance, from the arithmetic: the kernels work in fp32 and round once to bf16; the sum
+of squares over H terms is off by at most H * 2^-24 relative (6e-5 at H = 2048, far less
+in practice), exp and the division by a few fp32 ulps.  So every element must lie within
+one bf16 unit of the oracle (fp64, one rounding), and at most 1% of them (RMSNorm) or
+0.1% (residual sum, SiLU product) may differ from it at all."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from tests.gpu_helpers import bf16_dev, bits_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _key(bits):
+    b = bits.astype(np.int64)
+    return np.where(b >= 0x8000, -(b - 0x8000), b)
+
+
+def _within_one_ulp(got, want, frac, what):
+    d = np.abs(_key(got) - _key(want))
+    assert d.max(initial=0) <= 1, f"{what}: {int(d.max())} units off"
+    f = np.count_nonzero(d) / max(d.size, 1)
+    assert f <= frac, f"{what}: {f:.2e} of elements differ"
+
+
+@pytest.mark.parametrize("rows,hidden", [(4622, 2048), (37, 8), (5, 136), (3, 8192)])
+@pytest.mark.parametrize("with_res", [True, False])
+def test_residual_rmsnorm(rows, hidden, with_res):
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    _announce(f"residual_rmsnorm {rows}x{hidden} residual={with_res}")
+    x = W.normal_bf16([70, rows, hidden, 0], rows * hidden).reshape(rows, hidden)
+    r = W.normal_bf16([70, rows, hidden, 1], rows * hidden, 2.0).reshape(rows, hidden)
+    gm = W.normal_bf16([70, rows, hidden, 2], hidden)
+    xd, gd = bf16_dev(x), bf16_dev(gm)
+    out = torch.empty_like(xd)
+    rd = bf16_dev(r) if with_res else None
+    pa.residual_rmsnorm(xd, gd, out, residual_in=rd, residual_out=rd, eps=1e-5)  # in place
+    torch.cuda.synchronize()
+    want, h = O.residual_rmsnorm(x, r if with_res else None, gm, 1e-5)
+    if with_res:
+        _within_one_ulp(bits_host(rd), h, 1e-3, "residual sum")
+    _within_one_ulp(bits_host(out), want, 1e-2, "normalised rows")
+
+
+@pytest.mark.parametrize("rows,width,fused", [(4622, 8192, False), (4622, 8192, True),
+                                              (7, 1000, False), (1, 8, True)])
+def test_silu_mul(rows, width, fused):
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    _announce(f"silu_mul {rows}x{width} fused={fused}")
+    g = W.normal_bf16([71, rows, width, 0], rows * width, 3.0).reshape(rows, width)
+    u = W.normal_bf16([71, rows, width, 1], rows * width).reshape(rows, width)
+    if fused:  # one [rows, 2 width] gate|up buffer
+        gu = bf16_dev(np.concatenate([g, u], axis=1))
+        gd, ud = gu[:, :width], gu[:, width:]
+    else:
+        gd, ud = bf16_dev(g), bf16_dev(u)
+    out = torch.empty((rows, width), dtype=torch.bfloat16, device="cuda:0")
+    pa.silu_mul(gd, ud, out)
+    torch.cuda.synchronize()
+    _within_one_ulp(bits_host(out), O.silu_mul(g, u), 1e-3, "silu(g) * u")
