@@ -8,7 +8,8 @@ the one workload that runs every step of the path (append, decode partitions, sp
 merge, chunked prefill), so one step = one pass of the whole path.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload mixed|decode-long|decode-batched|prefill|rope-append|copy-pages]
+                    [--workload mixed|decode-long|decode-batched|prefill|rope-append|copy-pages|
+                                norm-mlp]
 
 Prints one JSON line.  ``value`` = decode KV bytes read per step / wall time per step
 (whole step, all kernels), the step captured once in a HIP graph and replayed (the eager
@@ -21,6 +22,9 @@ of the same workload (layer 0) before the GPU is touched.
 K/V append) on the 4608 new rows of the prefill workload, against HBM peak, with the
 plain pa_kv_append of the same rows beside it.  ``--workload copy-pages`` times
 pa_copy_pages (the copy half of copy-on-write) on 4096 block-size-32 pages of both pools.
+``--workload norm-mlp`` times pa_silu_mul on a concatenated [4622, 2 x 8192] gate|up buffer
+(the prefill workload's tokens at the 1B MLP width) with pa_residual_rmsnorm of the
+[4622, 2048] hidden rows beside it.
 """
 
 from __future__ import annotations
@@ -52,7 +56,14 @@ WORKLOADS = {
     "prefill": 3,
     "rope-append": 3,
     "copy-pages": 0,
+    "norm-mlp": 0,
 }
+NORM_ROWS, HIDDEN, MLP_WIDTH = 4622, 2048, 8192
+# Independent copies of a one-layer workload that a step walks through, so that its
+# working set (pools, q, outputs) exceeds the 256 MB last-level cache and every layer's
+# bytes come from HBM, as they do in the 16-layer mixed step.
+LAYER_COPIES = {2: 6, 3: 16}
+FLUSH_BYTES = 512 << 20  # read between kernel-level timed launches to evict the caches
 COPY_PAGES, COPY_BS = 4096, 32
 
 
@@ -161,7 +172,7 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
 
     dev = torch.device("cuda:0")
     lib = pa.library()
-    n_layers = W.NUM_LAYERS[cfg]
+    n_layers = max(W.NUM_LAYERS[cfg], LAYER_COPIES.get(cfg, 1))
     base = W.make_case(cfg, values=False)
     r_dec, r_pre = base.decode_seqs, base.prefill_seqs
     bt = torch.from_numpy(base.block_tables).to(dev)
@@ -173,7 +184,8 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     layers = []
     for li in range(n_layers):
         t0 = time.perf_counter()
-        case = W.fill_values(W.make_case(cfg, values=False), li)
+        case = W.fill_values(W.make_case(cfg, values=False), li % W.NUM_LAYERS[cfg] if
+                             cfg in LAYER_COPIES else li)
         layers.append(Layer(case, torch, pa, bt, ctx, cu_new, cu_q))
         del case
         torch.cuda.synchronize()
@@ -277,6 +289,27 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     return res
 
 
+def timed_launches(fn, steps: int, stream) -> float:
+    """Average HIP-event time of ``fn`` over ``steps`` launches, with FLUSH_BYTES of an
+    unrelated buffer read (summed) before each, so that no launch finds its inputs in the
+    L2s or the last-level cache.  The flush reads rather than writes: a written flush would
+    leave the cache full of dirty lines whose write-back the timed launch would pay for."""
+    import torch
+
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    ev = []
+    for _ in range(steps):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    del flush
+    return float(np.mean([x.elapsed_time(y) for x, y in ev]))
+
+
 def run_rope(cfg: int, steps: int, warmup: int) -> dict:
     """pa_rope_kv_append over the new rows of workload ``cfg`` (one layer), timed with HIP
     events per launch; pa_kv_append of the same rows timed the same way beside it."""
@@ -306,17 +339,6 @@ def run_rope(cfg: int, steps: int, warmup: int) -> dict:
         t, case.num_q_heads, case.head_dim)
     q_out = torch.empty_like(q)
 
-    def timed(fn, n):
-        ms = []
-        for _ in range(n):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            ms.append((a, b))
-        torch.cuda.synchronize()
-        return float(np.mean([x.elapsed_time(y) for x, y in ms]))
-
     rope = lambda: pa.rope_kv_append(geom, q, q_out, k_new, v_new, kp, vp, bt, cu, ctx,
                                      rope_theta=500000.0, stream=stream)
     plain = lambda: pa.kv_append(geom, k_new, v_new, kp, vp, bt, cu, ctx, stream=stream)
@@ -324,15 +346,13 @@ def run_rope(cfg: int, steps: int, warmup: int) -> dict:
         rope()
         plain()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    rope_ms = timed(rope, steps)
-    wall = time.perf_counter() - t0
-    plain_ms = timed(plain, steps)
+    rope_ms = timed_launches(rope, steps, stream)
+    plain_ms = timed_launches(plain, steps, stream)
     row = case.num_kv_heads * case.head_dim * 2  # bytes of one token's K (or V) row
     qrow = case.num_q_heads * case.head_dim * 2
     nbytes = t * (2 * qrow + 4 * row)  # q read + written, K/V read + written
     return {"rope_ms": rope_ms, "plain_ms": plain_ms, "bytes_per_launch": nbytes,
-            "plain_bytes_per_launch": t * 4 * row, "tokens": t, "ms_per_step": wall * 1e3 / steps,
+            "plain_bytes_per_launch": t * 4 * row, "tokens": t, "ms_per_step": rope_ms,
             "gbps": nbytes / (rope_ms * 1e-3) / 1e9,
             "plain_gbps": t * 4 * row / (plain_ms * 1e-3) / 1e9}
 
@@ -394,6 +414,8 @@ def main() -> int:
         return main_rope(args, cfg)
     if args.workload == "copy-pages":
         return main_copy(args)
+    if args.workload == "norm-mlp":
+        return main_norm(args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -403,7 +425,7 @@ def main() -> int:
 
     res = run_gpu(cfg, args.steps, args.warmup, args.partition)
     base = W.make_case(cfg, values=False)
-    config = {"workload": W.CONFIG_NAMES[cfg], "layers": W.NUM_LAYERS[cfg],
+    config = {"workload": W.CONFIG_NAMES[cfg], "layers": res["n_layers"],
               "block_size": base.block_size, "num_q_heads": 32, "num_kv_heads": 8,
               "head_dim": 64, "decode_seqs": len(base.decode_seqs),
               "prefill_seqs": len(base.prefill_seqs),
@@ -472,20 +494,11 @@ def run_copy(steps: int, warmup: int) -> dict:
     for _ in range(warmup):
         pa.copy_pages(geom, kp, vp, src, dst, stream=stream)
     torch.cuda.synchronize()
-    ev = []
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        pa.copy_pages(geom, kp, vp, src, dst, stream=stream)
-        b.record(stream)
-        ev.append((a, b))
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    ms = timed_launches(lambda: pa.copy_pages(geom, kp, vp, src, dst, stream=stream), steps,
+                        stream)
     nbytes = COPY_PAGES * e * 2 * 2 * 2  # both pools, read + written
     return {"ms": ms, "bytes_per_launch": nbytes, "gbps": nbytes / (ms * 1e-3) / 1e9,
-            "ms_per_step": wall * 1e3 / steps}
+            "ms_per_step": ms}
 
 
 def cpu_baseline_copy(budget_s: float) -> dict:
@@ -524,6 +537,81 @@ def main_copy(args) -> int:
                      "traffic": hbm_traffic("copy-pages"),
                      "bytes_per_launch": res["bytes_per_launch"],
                      "avg_launch_ms": round(res["ms"], 5)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_norm(steps: int, warmup: int) -> dict:
+    """pa_silu_mul and pa_residual_rmsnorm at the 1B shape, HIP-event timed per launch."""
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    dev = torch.device("cuda:0")
+    gu = torch.empty((NORM_ROWS, 2 * MLP_WIDTH), dtype=torch.bfloat16, device=dev).normal_()
+    act = torch.empty((NORM_ROWS, MLP_WIDTH), dtype=torch.bfloat16, device=dev)
+    x = torch.empty((NORM_ROWS, HIDDEN), dtype=torch.bfloat16, device=dev).normal_()
+    res = torch.empty_like(x).normal_()
+    gamma = torch.empty(HIDDEN, dtype=torch.bfloat16, device=dev).normal_()
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    silu = lambda: pa.silu_mul(gu[:, :MLP_WIDTH], gu[:, MLP_WIDTH:], act, stream=stream)
+    norm = lambda: pa.residual_rmsnorm(x, gamma, out, residual_in=res, residual_out=res,
+                                       stream=stream)
+
+    for _ in range(warmup):
+        silu()
+        norm()
+    silu_ms = timed_launches(silu, steps, stream)
+    norm_ms = timed_launches(norm, steps, stream)
+    silu_bytes = NORM_ROWS * MLP_WIDTH * 2 * 3      # gate, up read; product written
+    norm_bytes = NORM_ROWS * HIDDEN * 2 * 4         # x, residual read; residual, out written
+    return {"silu_ms": silu_ms, "silu_bytes": silu_bytes,
+            "silu_gbps": silu_bytes / (silu_ms * 1e-3) / 1e9, "norm_ms": norm_ms,
+            "norm_bytes": norm_bytes, "norm_gbps": norm_bytes / (norm_ms * 1e-3) / 1e9,
+            "ms_per_step": silu_ms}
+
+
+def cpu_baseline_norm(budget_s: float) -> dict:
+    """The oracle's SiLU product on a bounded slice of rows of the same shape."""
+    import oracle as O
+
+    rows = 64
+    g = W.normal_bf16([72, 0], rows * MLP_WIDTH).reshape(rows, MLP_WIDTH)
+    u = W.normal_bf16([72, 1], rows * MLP_WIDTH).reshape(rows, MLP_WIDTH)
+    t0, reps = time.perf_counter(), 0
+    while time.perf_counter() - t0 < min(budget_s, 5.0) or reps == 0:
+        O.silu_mul(g, u)
+        reps += 1
+    dt = time.perf_counter() - t0
+    return {"value": reps * rows * MLP_WIDTH * 6 / dt / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"fp64 numpy silu(g) * u oracle on {rows} x {MLP_WIDTH} x {reps} in "
+                      f"{dt:.1f} s, 1 thread"}
+
+
+def main_norm(args) -> int:
+    cpu = None if args.no_cpu_baseline else cpu_baseline_norm(args.cpu_budget)
+    res = run_norm(args.steps, args.warmup)
+    line = {
+        "metric": METRIC, "value": round(res["silu_gbps"], 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) bf16 activations and gamma)",
+        "config": {"workload": f"norm-mlp-{NORM_ROWS}x{HIDDEN}-mlp{MLP_WIDTH}", "layers": 1,
+                   "rows": NORM_ROWS, "hidden": HIDDEN, "mlp_width": MLP_WIDTH},
+        "roofline": {"bound": "hbm", "kernel": "pa_silu_mul (silu_mul_kernel)",
+                     "achieved": round(res["silu_gbps"], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(res["silu_gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": hbm_traffic("norm-mlp"), "bytes_per_launch": res["silu_bytes"],
+                     "avg_launch_ms": round(res["silu_ms"], 5)},
+        "residual_rmsnorm": {"kernel": "pa_residual_rmsnorm (residual_rmsnorm_kernel)",
+                             "bytes_per_launch": res["norm_bytes"],
+                             "avg_launch_ms": round(res["norm_ms"], 5),
+                             "achieved_gbps": round(res["norm_gbps"], 1),
+                             "frac": round(res["norm_gbps"] / HBM_PEAK_GBPS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

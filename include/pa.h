@@ -189,7 +189,8 @@ int pa_residual_rmsnorm(const void* x, const void* residual_in, void* residual_o
  * u = up[t*ld_in + j], in fp32, rounded once to bf16; written to out[t*ld_out + j], for
  * j < width.  A concatenated [n_rows][2*width] gate|up buffer is gate = base,
  * up = base + width, ld_in = 2*width.
- *   width, ld_in, ld_out    multiples of 8 with ld_in, ld_out >= width (elements)
+ *   width, ld_in, ld_out    multiples of 8 with ld_in, ld_out >= width (elements);
+ *                           width at most 2^24 (else PA_ERR_UNSUPPORTED)
  * PA_ERR_INVALID_ARG for a missing pointer or bad sizes.
  * ------------------------------------------------------------------------------- */
 int pa_silu_mul(const void* gate, const void* up, int64_t ld_in, void* out, int64_t ld_out,

@@ -295,6 +295,7 @@ int pa_silu_mul(const void* gate, const void* up, int64_t ld_in, void* out, int6
   if (n_rows < 0 || width <= 0 || width % 8 != 0) return PA_ERR_INVALID_ARG;
   if (ld_in < width || ld_out < width || ld_in % 8 != 0 || ld_out % 8 != 0)
     return PA_ERR_INVALID_ARG;
+  if (width > pa::silu_max_width()) return PA_ERR_UNSUPPORTED;
   if (n_rows == 0) return PA_OK;
   if (!gate || !up || !out) return PA_ERR_INVALID_ARG;
   return hip_status(pa::launch_silu_mul(gate, up, ld_in, out, ld_out, n_rows, width,

@@ -39,6 +39,8 @@ hipError_t launch_copy_pages(const LaunchGeom& geo, void* k_pool, void* v_pool,
 
 // Residual add + RMS normalisation of bf16 rows, and the SiLU-gated product.
 int rmsnorm_max_hidden();
+// Widest row pa_silu_mul takes: the column groups of a row go on grid axis y.
+int silu_max_width();
 hipError_t launch_residual_rmsnorm(const void* x, const void* residual_in, void* residual_out,
                                    const void* gamma, void* out, int n_rows, int hidden,
                                    float eps, hipStream_t stream);

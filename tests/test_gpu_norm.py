@@ -34,7 +34,11 @@ def _within_one_ulp(got, want, frac, what):
     assert f <= frac, f"{what}: {f:.2e} of elements differ"
 
 
-@pytest.mark.parametrize("rows,hidden", [(4622, 2048), (37, 8), (5, 136), (3, 8192)])
+# (4622, 2048): the 1B shape; the others reach every register budget of the kernel (rows
+# of up to 4, 8 and 16 chunks per lane), ragged chunk counts and row counts that leave a
+# workgroup part empty
+@pytest.mark.parametrize("rows,hidden", [(4622, 2048), (37, 8), (5, 136), (3, 8192),
+                                         (66, 2056), (9, 4096), (130, 6144)])
 @pytest.mark.parametrize("with_res", [True, False])
 def test_residual_rmsnorm(rows, hidden, with_res):
     import torch
@@ -56,8 +60,11 @@ def test_residual_rmsnorm(rows, hidden, with_res):
     _within_one_ulp(bits_host(out), want, 1e-2, "normalised rows")
 
 
+# enough rows for four chunks per thread (4622 x 8192, 600 x 8200 with a ragged last column
+# group) and too few (7 x 1000, 2 x 20000 over several column groups, 1 x 8)
 @pytest.mark.parametrize("rows,width,fused", [(4622, 8192, False), (4622, 8192, True),
-                                              (7, 1000, False), (1, 8, True)])
+                                              (600, 8200, True), (7, 1000, False),
+                                              (2, 20000, True), (1, 8, True)])
 def test_silu_mul(rows, width, fused):
     import torch
 
@@ -75,3 +82,21 @@ def test_silu_mul(rows, width, fused):
     pa.silu_mul(gd, ud, out)
     torch.cuda.synchronize()
     _within_one_ulp(bits_host(out), O.silu_mul(g, u), 1e-3, "silu(g) * u")
+
+
+def test_silu_mul_strided_out():
+    """The product written into the left half of a wider buffer; the right half untouched."""
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    rows, width = 513, 3072
+    _announce(f"silu_mul {rows}x{width} into a [{rows}, {2 * width}] buffer")
+    g = W.normal_bf16([71, rows, width, 2], rows * width, 3.0).reshape(rows, width)
+    u = W.normal_bf16([71, rows, width, 3], rows * width).reshape(rows, width)
+    wide = torch.full((rows, 2 * width), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    pa.silu_mul(bf16_dev(g), bf16_dev(u), wide[:, :width])
+    torch.cuda.synchronize()
+    host = bits_host(wide)
+    _within_one_ulp(host[:, :width], O.silu_mul(g, u), 1e-3, "silu(g) * u")
+    assert np.all(host[:, width:] == W.f32_to_bf16_bits(np.float32([7.0]))[0])
