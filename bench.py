@@ -19,12 +19,18 @@ against dense bf16 MFMA peak.  ``cpu_baseline`` times the CPU oracle on a bounde
 of the same workload (layer 0) before the GPU is touched.
 
 ``--workload rope-append`` times pa_rope_kv_append alone (RoPE of Q and K fused with the
-K/V append) on the 4608 new rows of the prefill workload, against HBM peak, with the
+K/V append) on the 4622 new rows of the prefill workload, against HBM peak, with the
 plain pa_kv_append of the same rows beside it.  ``--workload copy-pages`` times
 pa_copy_pages (the copy half of copy-on-write) on 4096 block-size-32 pages of both pools.
 ``--workload norm-mlp`` times pa_silu_mul on a concatenated [4622, 2 x 8192] gate|up buffer
 (the prefill workload's tokens at the 1B MLP width) with pa_residual_rmsnorm of the
 [4622, 2048] hidden rows beside it.
+
+No timed launch finds its inputs in a cache: the decode-batched and prefill workloads (one
+layer each) walk through 6 and 16 independent copies of their layer, and the kernel-level
+workloads cycle back-to-back launches through independent buffer sets of at least 1 GiB
+in total, four times the last-level cache, so each launch also pays for the write-back of
+the outputs before it, as in a layer-by-layer pass.
 """
 
 from __future__ import annotations
@@ -63,7 +69,10 @@ NORM_ROWS, HIDDEN, MLP_WIDTH = 4622, 2048, 8192
 # working set (pools, q, outputs) exceeds the 256 MB last-level cache and every layer's
 # bytes come from HBM, as they do in the 16-layer mixed step.
 LAYER_COPIES = {2: 6, 3: 16}
-FLUSH_BYTES = 512 << 20  # read between kernel-level timed launches to evict the caches
+# Kernel-level workloads rotate over independent copies of their buffers totalling at least
+# this many bytes, so that back-to-back launches find nothing in the L2s or the 256 MB
+# last-level cache and pay for the write-back of the launches before them, as a layer does.
+ROTATE_BYTES = 1 << 30
 COPY_PAGES, COPY_BS = 4096, 32
 
 
@@ -289,24 +298,26 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     return res
 
 
-def timed_launches(fn, steps: int, stream) -> float:
-    """Average HIP-event time of ``fn`` over ``steps`` launches, with FLUSH_BYTES of an
-    unrelated buffer read (summed) before each, so that no launch finds its inputs in the
-    L2s or the last-level cache.  The flush reads rather than writes: a written flush would
-    leave the cache full of dirty lines whose write-back the timed launch would pay for."""
+def n_copies(footprint: int) -> int:
+    """Independent buffer sets a kernel-level workload rotates over (at least two)."""
+    return max(2, -(-ROTATE_BYTES // max(footprint, 1)))
+
+
+def timed_rotating(fns, steps: int, stream) -> float:
+    """Average HIP-event time of one launch over ``steps`` back-to-back launches that
+    cycle through ``fns`` (one closure per buffer set)."""
     import torch
 
-    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    for fn in fns:
+        fn()
     ev = []
-    for _ in range(steps):
-        flush.sum()
+    for i in range(steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        fn()
+        fns[i % len(fns)]()
         b.record(stream)
         ev.append((a, b))
     torch.cuda.synchronize()
-    del flush
     return float(np.mean([x.elapsed_time(y) for x, y in ev]))
 
 
@@ -328,31 +339,37 @@ def run_rope(cfg: int, steps: int, warmup: int) -> dict:
     geom = pa.Geometry(case.num_pages, case.block_size, case.num_q_heads, case.num_kv_heads,
                        case.head_dim)
     e = W.page_elems(case)
-    kp = torch.zeros((case.num_pages, e), dtype=torch.bfloat16, device=dev)
-    vp = torch.zeros_like(kp)
     bt = torch.from_numpy(case.block_tables).to(dev)
     ctx = torch.from_numpy(case.ctx_lens).to(dev)
     cu = torch.from_numpy(case.cu_new_lens).to(dev)
-    k_new, v_new = up16(case.k_new), up16(case.v_new)
+    k0, v0 = up16(case.k_new), up16(case.v_new)
     t = int(case.k_new.shape[0])
-    q = up16(W.normal_bf16([77, cfg], t * case.num_q_heads * case.head_dim)).view(
+    q0 = up16(W.normal_bf16([77, cfg], t * case.num_q_heads * case.head_dim)).view(
         t, case.num_q_heads, case.head_dim)
-    q_out = torch.empty_like(q)
-
-    rope = lambda: pa.rope_kv_append(geom, q, q_out, k_new, v_new, kp, vp, bt, cu, ctx,
-                                     rope_theta=500000.0, stream=stream)
-    plain = lambda: pa.kv_append(geom, k_new, v_new, kp, vp, bt, cu, ctx, stream=stream)
-    for _ in range(warmup):
-        rope()
-        plain()
-    torch.cuda.synchronize()
-    rope_ms = timed_launches(rope, steps, stream)
-    plain_ms = timed_launches(plain, steps, stream)
     row = case.num_kv_heads * case.head_dim * 2  # bytes of one token's K (or V) row
     qrow = case.num_q_heads * case.head_dim * 2
+    footprint = 2 * case.num_pages * e * 2 + t * (2 * qrow + 2 * row)
+    ropes, plains = [], []
+    for _ in range(n_copies(footprint)):
+        kp = torch.zeros((case.num_pages, e), dtype=torch.bfloat16, device=dev)
+        vp = torch.zeros_like(kp)
+        q, k_new, v_new = q0.clone(), k0.clone(), v0.clone()
+        q_out = torch.empty_like(q)
+        ropes.append(lambda q=q, q_out=q_out, k_new=k_new, v_new=v_new, kp=kp, vp=vp:
+                     pa.rope_kv_append(geom, q, q_out, k_new, v_new, kp, vp, bt, cu, ctx,
+                                       rope_theta=500000.0, stream=stream))
+        plains.append(lambda k_new=k_new, v_new=v_new, kp=kp, vp=vp:
+                      pa.kv_append(geom, k_new, v_new, kp, vp, bt, cu, ctx, stream=stream))
+    for _ in range(warmup):
+        ropes[0]()
+        plains[0]()
+    torch.cuda.synchronize()
+    rope_ms = timed_rotating(ropes, steps, stream)
+    plain_ms = timed_rotating(plains, steps, stream)
     nbytes = t * (2 * qrow + 4 * row)  # q read + written, K/V read + written
     return {"rope_ms": rope_ms, "plain_ms": plain_ms, "bytes_per_launch": nbytes,
             "plain_bytes_per_launch": t * 4 * row, "tokens": t, "ms_per_step": rope_ms,
+            "buffer_sets": len(ropes),
             "gbps": nbytes / (rope_ms * 1e-3) / 1e9,
             "plain_gbps": t * 4 * row / (plain_ms * 1e-3) / 1e9}
 
@@ -484,21 +501,23 @@ def run_copy(steps: int, warmup: int) -> dict:
     dev = torch.device("cuda:0")
     n_pages = 2 * COPY_PAGES
     e = COPY_BS * 8 * 64
-    kp = torch.empty((n_pages, e), dtype=torch.bfloat16, device=dev).normal_()
-    vp = torch.empty_like(kp).normal_()
+    pools = [(torch.empty((n_pages, e), dtype=torch.bfloat16, device=dev).normal_(),
+              torch.empty((n_pages, e), dtype=torch.bfloat16, device=dev).normal_())
+             for _ in range(n_copies(2 * n_pages * e * 2))]
     perm = np.random.default_rng(7).permutation(n_pages).astype(np.int32)
     src = torch.from_numpy(perm[:COPY_PAGES].copy()).to(dev)
     dst = torch.from_numpy(perm[COPY_PAGES:].copy()).to(dev)
     geom = pa.Geometry(n_pages, COPY_BS, 32, 8, 64)
     stream = torch.cuda.current_stream()
+    fns = [lambda kp=kp, vp=vp: pa.copy_pages(geom, kp, vp, src, dst, stream=stream)
+           for kp, vp in pools]
     for _ in range(warmup):
-        pa.copy_pages(geom, kp, vp, src, dst, stream=stream)
+        fns[0]()
     torch.cuda.synchronize()
-    ms = timed_launches(lambda: pa.copy_pages(geom, kp, vp, src, dst, stream=stream), steps,
-                        stream)
+    ms = timed_rotating(fns, steps, stream)
     nbytes = COPY_PAGES * e * 2 * 2 * 2  # both pools, read + written
     return {"ms": ms, "bytes_per_launch": nbytes, "gbps": nbytes / (ms * 1e-3) / 1e9,
-            "ms_per_step": ms}
+            "ms_per_step": ms, "buffer_sets": len(fns)}
 
 
 def cpu_baseline_copy(budget_s: float) -> dict:
@@ -530,7 +549,8 @@ def main_copy(args) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (N(0,1) bf16 pools, seeded page permutation)",
         "config": {"workload": f"copy-pages-{COPY_PAGES}x-bs{COPY_BS}", "layers": 1,
-                   "block_size": COPY_BS, "num_kv_heads": 8, "head_dim": 64},
+                   "block_size": COPY_BS, "num_kv_heads": 8, "head_dim": 64,
+                   "buffer_sets": res["buffer_sets"]},
         "roofline": {"bound": "hbm", "kernel": "pa_copy_pages (copy_pages_kernel)",
                      "achieved": round(res["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(res["gbps"] / HBM_PEAK_GBPS, 4),
@@ -550,28 +570,32 @@ def run_norm(steps: int, warmup: int) -> dict:
     import paged_kv_attention_31_amd as pa
 
     dev = torch.device("cuda:0")
-    gu = torch.empty((NORM_ROWS, 2 * MLP_WIDTH), dtype=torch.bfloat16, device=dev).normal_()
-    act = torch.empty((NORM_ROWS, MLP_WIDTH), dtype=torch.bfloat16, device=dev)
-    x = torch.empty((NORM_ROWS, HIDDEN), dtype=torch.bfloat16, device=dev).normal_()
-    res = torch.empty_like(x).normal_()
-    gamma = torch.empty(HIDDEN, dtype=torch.bfloat16, device=dev).normal_()
-    out = torch.empty_like(x)
     stream = torch.cuda.current_stream()
-    silu = lambda: pa.silu_mul(gu[:, :MLP_WIDTH], gu[:, MLP_WIDTH:], act, stream=stream)
-    norm = lambda: pa.residual_rmsnorm(x, gamma, out, residual_in=res, residual_out=res,
-                                       stream=stream)
-
-    for _ in range(warmup):
-        silu()
-        norm()
-    silu_ms = timed_launches(silu, steps, stream)
-    norm_ms = timed_launches(norm, steps, stream)
     silu_bytes = NORM_ROWS * MLP_WIDTH * 2 * 3      # gate, up read; product written
     norm_bytes = NORM_ROWS * HIDDEN * 2 * 4         # x, residual read; residual, out written
+    silus, norms = [], []
+    for _ in range(n_copies(silu_bytes)):
+        gu = torch.empty((NORM_ROWS, 2 * MLP_WIDTH), dtype=torch.bfloat16, device=dev).normal_()
+        act = torch.empty((NORM_ROWS, MLP_WIDTH), dtype=torch.bfloat16, device=dev)
+        silus.append(lambda gu=gu, act=act: pa.silu_mul(gu[:, :MLP_WIDTH], gu[:, MLP_WIDTH:], act,
+                                                        stream=stream))
+    gamma = torch.empty(HIDDEN, dtype=torch.bfloat16, device=dev).normal_()
+    for _ in range(n_copies(norm_bytes - NORM_ROWS * HIDDEN * 2)):
+        x = torch.empty((NORM_ROWS, HIDDEN), dtype=torch.bfloat16, device=dev).normal_()
+        res = torch.empty_like(x).normal_()
+        out = torch.empty_like(x)
+        norms.append(lambda x=x, res=res, out=out: pa.residual_rmsnorm(
+            x, gamma, out, residual_in=res, residual_out=res, stream=stream))
+
+    for _ in range(warmup):
+        silus[0]()
+        norms[0]()
+    silu_ms = timed_rotating(silus, steps, stream)
+    norm_ms = timed_rotating(norms, steps, stream)
     return {"silu_ms": silu_ms, "silu_bytes": silu_bytes,
             "silu_gbps": silu_bytes / (silu_ms * 1e-3) / 1e9, "norm_ms": norm_ms,
             "norm_bytes": norm_bytes, "norm_gbps": norm_bytes / (norm_ms * 1e-3) / 1e9,
-            "ms_per_step": silu_ms}
+            "ms_per_step": silu_ms, "buffer_sets": [len(silus), len(norms)]}
 
 
 def cpu_baseline_norm(budget_s: float) -> dict:
@@ -601,7 +625,8 @@ def main_norm(args) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (N(0,1) bf16 activations and gamma)",
         "config": {"workload": f"norm-mlp-{NORM_ROWS}x{HIDDEN}-mlp{MLP_WIDTH}", "layers": 1,
-                   "rows": NORM_ROWS, "hidden": HIDDEN, "mlp_width": MLP_WIDTH},
+                   "rows": NORM_ROWS, "hidden": HIDDEN, "mlp_width": MLP_WIDTH,
+                   "buffer_sets": res["buffer_sets"]},
         "roofline": {"bound": "hbm", "kernel": "pa_silu_mul (silu_mul_kernel)",
                      "achieved": round(res["silu_gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(res["silu_gbps"] / HBM_PEAK_GBPS, 4),
@@ -670,7 +695,8 @@ def main_rope(args, cfg: int) -> int:
         "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shuffled pages)",
         "config": {"workload": f"rope-append-{res['tokens']}tokens-bs{base.block_size}",
                    "layers": 1, "block_size": base.block_size, "num_q_heads": 32,
-                   "num_kv_heads": 8, "head_dim": 64, "rope_theta": 500000.0},
+                   "num_kv_heads": 8, "head_dim": 64, "rope_theta": 500000.0,
+                   "buffer_sets": res["buffer_sets"]},
         "roofline": {"bound": "hbm", "kernel": "pa_rope_kv_append (append_kernel<bs, rope>)",
                      "achieved": round(res["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(res["gbps"] / HBM_PEAK_GBPS, 4),
