@@ -104,6 +104,8 @@ int pa_pool_create(int32_t num_pages, pa_pool_t** out);
 void pa_pool_destroy(pa_pool_t* p);
 
 /* Take `n` pages off the free list into ids_out[0..n-1], each with reference count 1.
+ * The free list is a stack: a fresh pool hands out 0, 1, 2, ... in that order, and a
+ * page that returns to it is the next one handed out.
  * All or nothing: PA_ERR_OUT_OF_PAGES leaves the pool unchanged. */
 int pa_pool_alloc(pa_pool_t* p, int32_t n, int32_t* ids_out);
 
@@ -302,6 +304,84 @@ int pa_prefill(pa_geom_t g, void* out, const void* q, const void* k_pool, const 
                const int32_t* cu_q_lens, const int32_t* ctx_lens, int32_t n_seqs,
                int32_t max_q_len, int32_t max_ctx_len, float scale, int32_t causal,
                int32_t kv_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Slot scheduler: continuous batching as [实战] §连续批处理：吞吐与延迟的平衡 describes it.
+ * The batch is a fixed set of `num_slots` slots, one request each; a request goes
+ * waiting -> prefill -> decode -> done; a freed slot takes the next queued request; a
+ * prefill step runs on its own, a decode step runs every decoding slot, and the two
+ * alternate while both have work, so a long prompt cannot stall decoding.  Pages come
+ * from `pool` only when a step first writes into them ([guide] §PagedAttention).
+ * Host only: it launches nothing and touches no device memory.  Calls on one scheduler
+ * are serialised internally.
+ *
+ * pa_sched_step, in order:
+ *   1. retires every request that has produced max_new_tokens tokens or was passed to
+ *      pa_sched_finish: its pages go back to the pool, its id is written to finished[];
+ *   2. admits queued requests, oldest first, into the lowest free slots while the pool's
+ *      free pages, less the pages still promised to admitted requests, cover the next
+ *      request's worst case ceil((prompt_len + max_new_tokens - 1) / block_size); the
+ *      first request that does not fit stops admission (no overtaking);
+ *   3. chooses the kind: PA_STEP_PREFILL if some slot is prefilling and either none is
+ *      decoding or the previous step was not a prefill step; else PA_STEP_DECODE if some
+ *      slot is decoding; else PA_STEP_IDLE;
+ *   4. prefill: prefilling slots in admission order take their remaining prompt tokens
+ *      until prefill_chunk tokens are given out; a slot whose prompt completes has
+ *      produced its first token and decodes from the next step on;
+ *   5. decode: every decoding slot appends one token (its latest) and produces the next.
+ * Row k of the step (k < n_seqs, admission order) is request req_ids[k] in slot
+ * slots[k]; it appends rows cu_new_lens[k] .. cu_new_lens[k+1]-1 at positions
+ * ctx_lens[k] - n_k .. ctx_lens[k] - 1 and then attends over ctx_lens[k] tokens through
+ * block_tables[k][0 .. ceil(ctx_lens[k]/block_size) - 1] (entries past that are -1).
+ * These are the arguments of pa_kv_append / pa_rope_kv_append, then pa_prefill
+ * (cu_q_lens = cu_new_lens, max_q_len = info->max_new_len) or pa_decode, once copied to
+ * the device.  A request produces its tokens over one prefill pass of prompt_len tokens
+ * and max_new_tokens - 1 decode steps; the token values belong to the caller.
+ * ------------------------------------------------------------------------------- */
+typedef struct pa_sched pa_sched_t;
+
+enum { PA_STEP_IDLE = 0, PA_STEP_PREFILL = 1, PA_STEP_DECODE = 2 };
+
+typedef struct pa_sched_step {
+  int32_t kind;         /* PA_STEP_* */
+  int32_t n_seqs;       /* rows in this step */
+  int32_t n_new_tokens; /* cu_new_lens[n_seqs] */
+  int32_t max_ctx_len;  /* largest ctx_lens[k] */
+  int32_t max_new_len;  /* largest n_k (max_q_len for pa_prefill) */
+  int32_t n_finished;   /* ids written to finished[] */
+} pa_sched_step_t;
+
+/* Create a scheduler over `pool`, which must outlive it (other users may share the pool:
+ * admission counts its free pages at every step).  num_slots, block_size (tokens per
+ * page), max_blocks_per_seq (the length of a block-table row) and prefill_chunk (prompt
+ * tokens per prefill step) must be >= 1, else PA_ERR_INVALID_ARG. */
+int pa_sched_create(pa_pool_t* pool, int32_t num_slots, int32_t block_size,
+                    int32_t max_blocks_per_seq, int32_t prefill_chunk, pa_sched_t** out);
+
+/* Destroy a scheduler; pages held by its requests go back to the pool (NULL ignored). */
+void pa_sched_destroy(pa_sched_t* s);
+
+/* Queue a request.  PA_ERR_INVALID_ARG for prompt_len < 1, max_new_tokens < 1 or an id
+ * already queued or active; PA_ERR_UNSUPPORTED when its worst case needs more than
+ * max_blocks_per_seq pages (it could never run).  Nothing changes on error. */
+int pa_sched_submit(pa_sched_t* s, int64_t req_id, int32_t prompt_len, int32_t max_new_tokens);
+
+/* Stop a request early (say, at an end-of-sequence token): a queued one leaves the queue
+ * at once; an active one is retired by the next step.  PA_ERR_INVALID_ARG if unknown. */
+int pa_sched_finish(pa_sched_t* s, int64_t req_id);
+
+/* Requests queued or active (-1 for NULL). */
+int32_t pa_sched_pending(const pa_sched_t* s);
+
+/* Decide and record the next step (see above).  Caller-owned host arrays, capacities:
+ * req_ids, slots, ctx_lens, finished: num_slots; cu_new_lens: num_slots + 1;
+ * block_tables: num_slots * max_blocks_per_seq.  PA_ERR_INVALID_ARG for a NULL pointer.
+ * PA_ERR_OUT_OF_PAGES only when another user of the pool took pages promised to admitted
+ * requests: then the retirements and admissions of the call stand (finished[] and
+ * info->n_finished are filled), no tokens are scheduled and info->kind is PA_STEP_IDLE. */
+int pa_sched_step(pa_sched_t* s, pa_sched_step_t* info, int64_t* req_ids, int32_t* slots,
+                  int32_t* block_tables, int32_t* ctx_lens, int32_t* cu_new_lens,
+                  int64_t* finished);
 
 #ifdef __cplusplus
 }

@@ -16,12 +16,15 @@ from __future__ import annotations
 
 import ctypes
 import dataclasses
-from typing import Optional, Sequence
+from typing import NamedTuple, Optional, Sequence
+
+import numpy as np
 
 from . import _lib
 
 __all__ = [
-    "PagedAttnError", "Geometry", "PagePool", "page_bytes", "kv_append", "rope_kv_append",
+    "PagedAttnError", "Geometry", "PagePool", "Scheduler", "StepPlan", "STEP_IDLE",
+    "STEP_PREFILL", "STEP_DECODE", "page_bytes", "kv_append", "rope_kv_append",
     "copy_pages", "residual_rmsnorm", "silu_mul",
     "decode_partition_tokens", "decode_workspace_bytes", "decode", "prefill_workspace_bytes",
     "prefill", "library",
@@ -120,6 +123,78 @@ class PagePool:
 
     def refcount(self, page: int) -> int:
         return int(self._lib.pa_pool_refcount(self._h, int(page)))
+
+
+STEP_IDLE, STEP_PREFILL, STEP_DECODE = _lib.PA_STEP_IDLE, _lib.PA_STEP_PREFILL, _lib.PA_STEP_DECODE
+
+
+class StepPlan(NamedTuple):
+    """One scheduler step (see pa_sched_step): host numpy arrays, row k = request
+    req_ids[k] in slot slots[k]."""
+
+    kind: int
+    req_ids: np.ndarray       # int64 [n]
+    slots: np.ndarray         # int32 [n]
+    block_tables: np.ndarray  # int32 [n, max_blocks_per_seq], -1 past the used pages
+    ctx_lens: np.ndarray      # int32 [n]
+    cu_new_lens: np.ndarray   # int32 [n + 1]
+    max_ctx_len: int
+    max_new_len: int
+    finished: np.ndarray      # int64 ids retired at the start of the step
+
+
+class Scheduler:
+    """Slot scheduler over a PagePool (see pa_sched_*): host decisions only."""
+
+    def __init__(self, pool: PagePool, num_slots: int, block_size: int,
+                 max_blocks_per_seq: int, prefill_chunk: int):
+        self._lib = _lib.load()
+        self._pool = pool  # the pool must outlive the scheduler
+        h = ctypes.c_void_p()
+        _check(self._lib.pa_sched_create(pool._h, int(num_slots), int(block_size),
+                                         int(max_blocks_per_seq), int(prefill_chunk),
+                                         ctypes.byref(h)), "pa_sched_create")
+        self._h = h
+        self.num_slots, self.max_blocks = int(num_slots), int(max_blocks_per_seq)
+        self._req = np.zeros(self.num_slots, np.int64)
+        self._slots = np.zeros(self.num_slots, np.int32)
+        self._bt = np.zeros((self.num_slots, self.max_blocks), np.int32)
+        self._ctx = np.zeros(self.num_slots, np.int32)
+        self._cu = np.zeros(self.num_slots + 1, np.int32)
+        self._fin = np.zeros(self.num_slots, np.int64)
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pa_sched_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, req_id: int, prompt_len: int, max_new_tokens: int) -> None:
+        _check(self._lib.pa_sched_submit(self._h, int(req_id), int(prompt_len),
+                                         int(max_new_tokens)), "pa_sched_submit")
+
+    def finish(self, req_id: int) -> None:
+        _check(self._lib.pa_sched_finish(self._h, int(req_id)), "pa_sched_finish")
+
+    def pending(self) -> int:
+        return int(self._lib.pa_sched_pending(self._h))
+
+    def step(self) -> StepPlan:
+        info = _lib.PaSchedStep()
+        p = lambda a: a.ctypes.data
+        _check(self._lib.pa_sched_step(self._h, ctypes.byref(info), p(self._req), p(self._slots),
+                                       p(self._bt), p(self._ctx), p(self._cu), p(self._fin)),
+               "pa_sched_step")
+        n = int(info.n_seqs)
+        return StepPlan(int(info.kind), self._req[:n].copy(), self._slots[:n].copy(),
+                        self._bt[:n].copy(), self._ctx[:n].copy(), self._cu[:n + 1].copy(),
+                        int(info.max_ctx_len), int(info.max_new_len),
+                        self._fin[:int(info.n_finished)].copy())
 
 
 # ---------------------------------------------------------------------------------------

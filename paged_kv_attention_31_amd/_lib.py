@@ -26,6 +26,19 @@ class PaGeom(ctypes.Structure):
     ]
 
 
+class PaSchedStep(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("n_seqs", ctypes.c_int32),
+        ("n_new_tokens", ctypes.c_int32),
+        ("max_ctx_len", ctypes.c_int32),
+        ("max_new_len", ctypes.c_int32),
+        ("n_finished", ctypes.c_int32),
+    ]
+
+
+PA_STEP_IDLE, PA_STEP_PREFILL, PA_STEP_DECODE = 0, 1, 2
+
 _c_i32 = ctypes.c_int32
 _c_p = ctypes.c_void_p
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
@@ -45,6 +58,14 @@ SIGNATURES = {
     "pa_pool_cow": (ctypes.c_int, [_c_p, _c_i32, _c_i32p, _c_i32p]),
     "pa_pool_num_free": (_c_i32, [_c_p]),
     "pa_pool_refcount": (_c_i32, [_c_p, _c_i32]),
+    "pa_sched_create": (ctypes.c_int, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32,
+                                       ctypes.POINTER(_c_p)]),
+    "pa_sched_destroy": (None, [_c_p]),
+    "pa_sched_submit": (ctypes.c_int, [_c_p, ctypes.c_int64, _c_i32, _c_i32]),
+    "pa_sched_finish": (ctypes.c_int, [_c_p, ctypes.c_int64]),
+    "pa_sched_pending": (_c_i32, [_c_p]),
+    "pa_sched_step": (ctypes.c_int, [_c_p, ctypes.POINTER(PaSchedStep), _c_p, _c_p, _c_p, _c_p,
+                                     _c_p, _c_p]),
     "pa_kv_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p,
                                     _c_i32, _c_i32, _c_p]),
     "pa_copy_pages": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p]),

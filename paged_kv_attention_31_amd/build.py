@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["abi.cpp", "append.hip", "decode.hip", "prefill.hip", "norm.hip"]
+SOURCES = ["abi.cpp", "sched.cpp", "append.hip", "decode.hip", "prefill.hip", "norm.hip"]
 ARCH = "gfx950"
 
 
