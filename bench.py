@@ -9,7 +9,7 @@ merge, chunked prefill), so one step = one pass of the whole path.
 
     python bench.py [--steps K] [--warmup W]
                     [--workload mixed|decode-long|decode-batched|prefill|rope-append|copy-pages|
-                                norm-mlp]
+                                norm-mlp|serve]
 
 Prints one JSON line.  ``value`` = decode KV bytes read per step / wall time per step
 (whole step, all kernels), the step captured once in a HIP graph and replayed (the eager
@@ -24,7 +24,11 @@ plain pa_kv_append of the same rows beside it.  ``--workload copy-pages`` times
 pa_copy_pages (the copy half of copy-on-write) on 4096 block-size-32 pages of both pools.
 ``--workload norm-mlp`` times pa_silu_mul on a concatenated [4622, 2 x 8192] gate|up buffer
 (the prefill workload's tokens at the 1B MLP width) with pa_residual_rmsnorm of the
-[4622, 2048] hidden rows beside it.
+[4622, 2048] hidden rows beside it.  ``--workload serve`` runs the slot scheduler
+(pa_sched_step) over 256 requests (prompts U[128, 1024], U[16, 128] new tokens, 64 slots,
+16 layers), each plan uploaded and run through pa_kv_append + pa_prefill / pa_decode;
+``value`` is the decode KV-read rate over the scheduled decode launches, with the
+scheduler's host time per step and the generated tokens per second of the whole loop.
 
 No timed launch finds its inputs in a cache: the decode-batched and prefill workloads (one
 layer each) walk through 6 and 16 independent copies of their layer, and the kernel-level
@@ -63,6 +67,7 @@ WORKLOADS = {
     "rope-append": 3,
     "copy-pages": 0,
     "norm-mlp": 0,
+    "serve": 0,
 }
 NORM_ROWS, HIDDEN, MLP_WIDTH = 4622, 2048, 8192
 # Independent copies of a one-layer workload that a step walks through, so that its
@@ -74,6 +79,9 @@ LAYER_COPIES = {2: 6, 3: 16}
 # last-level cache and pay for the write-back of the launches before them, as a layer does.
 ROTATE_BYTES = 1 << 30
 COPY_PAGES, COPY_BS = 4096, 32
+# scheduler-driven serving run: requests with prompts U[128, 1024] (the prefill workload's
+# range) and U[16, 128] new tokens through 64 slots, 16 layers, block size 16
+SERVE_REQS, SERVE_SLOTS, SERVE_CHUNK, SERVE_BS, SERVE_LAYERS = 256, 64, 2048, 16, 16
 
 
 def log(msg: str) -> None:
@@ -433,6 +441,8 @@ def main() -> int:
         return main_copy(args)
     if args.workload == "norm-mlp":
         return main_norm(args)
+    if args.workload == "serve":
+        return main_serve(args)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -614,6 +624,168 @@ def cpu_baseline_norm(budget_s: float) -> dict:
             "kind": "oracle",
             "sample": f"fp64 numpy silu(g) * u oracle on {rows} x {MLP_WIDTH} x {reps} in "
                       f"{dt:.1f} s, 1 thread"}
+
+
+def serve_stream():
+    rng = np.random.default_rng([93, 0])
+    return (rng.integers(128, 1025, SERVE_REQS).tolist(), rng.integers(16, 129, SERVE_REQS).tolist())
+
+
+def run_serve() -> dict:
+    """The slot scheduler (pa_sched_step) driving pa_kv_append + pa_prefill / pa_decode on
+    each of SERVE_LAYERS layers over SERVE_REQS requests until all have finished: every
+    plan is uploaded once and run as is.
+    Kernels are timed with HIP events; the scheduler's own host time is measured apart."""
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    dev = torch.device("cuda:0")
+    prompts, news = serve_stream()
+    max_blocks = -(-(1024 + 128 - 1) // SERVE_BS)
+    n_pages = int(SERVE_SLOTS * max_blocks * 1.1)
+    geom = pa.Geometry(n_pages, SERVE_BS, 32, 8, 64)
+    e = SERVE_BS * 8 * 64
+    pools = [(torch.empty((n_pages, e), dtype=torch.bfloat16, device=dev).normal_(),
+              torch.empty((n_pages, e), dtype=torch.bfloat16, device=dev).normal_())
+             for _ in range(SERVE_LAYERS)]
+    rows_max = max(SERVE_CHUNK, SERVE_SLOTS)
+    k_src = torch.empty((rows_max, 8, 64), dtype=torch.bfloat16, device=dev).normal_()
+    v_src = torch.empty_like(k_src).normal_()
+    q_src = torch.empty((rows_max, 32, 64), dtype=torch.bfloat16, device=dev).normal_()
+    out = torch.empty_like(q_src)
+    pool = pa.PagePool(n_pages)
+    sched = pa.Scheduler(pool, SERVE_SLOTS, SERVE_BS, max_blocks, SERVE_CHUNK)
+    for rid, (p, m) in enumerate(zip(prompts, news)):
+        sched.submit(rid, p, m)
+    stream = torch.cuda.current_stream()
+    ev = {pa.STEP_PREFILL: [], pa.STEP_DECODE: []}
+    kv_bytes = pairs = 0
+    n_steps = {pa.STEP_PREFILL: 0, pa.STEP_DECODE: 0}
+    sched_s = 0.0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        a = time.perf_counter()
+        plan = sched.step()
+        sched_s += time.perf_counter() - a
+        if plan.kind == pa.STEP_IDLE:
+            if sched.pending() == 0:
+                break
+            continue
+        n = len(plan.req_ids)
+        t = int(plan.cu_new_lens[-1])
+        bt = torch.from_numpy(plan.block_tables).to(dev)
+        ctx = torch.from_numpy(plan.ctx_lens).to(dev)
+        cu = torch.from_numpy(plan.cu_new_lens).to(dev)
+        for kp, vp in pools:  # one block table serves every layer
+            pa.kv_append(geom, k_src[:t], v_src[:t], kp, vp, bt, cu, ctx, stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if plan.kind == pa.STEP_PREFILL:
+                pa.prefill(geom, out[:t], q_src[:t], kp, vp, bt, cu, ctx, plan.max_new_len,
+                           plan.max_ctx_len, 0.125, causal=True, stream=stream)
+            else:
+                pa.decode(geom, out[:n], q_src[:n], kp, vp, bt, ctx, plan.max_ctx_len, 0.125,
+                          stream=stream)
+            e1.record(stream)
+            ev[plan.kind].append((e0, e1))
+        if plan.kind == pa.STEP_PREFILL:
+            lens = np.diff(plan.cu_new_lens).astype(np.int64)
+            c = plan.ctx_lens.astype(np.int64)
+            pairs += SERVE_LAYERS * int(np.sum(lens * (c - lens) + lens * (lens + 1) // 2))
+        else:
+            kv_bytes += (SERVE_LAYERS * int(plan.ctx_lens.astype(np.int64).sum())
+                         * KV_BYTES_PER_TOKEN)
+        n_steps[plan.kind] += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sched.close()
+    dec_ms = sum(x.elapsed_time(y) for x, y in ev[pa.STEP_DECODE])
+    pre_ms = sum(x.elapsed_time(y) for x, y in ev[pa.STEP_PREFILL])
+    steps = n_steps[pa.STEP_PREFILL] + n_steps[pa.STEP_DECODE]
+    return {"wall_s": wall, "steps": steps, "prefill_steps": n_steps[pa.STEP_PREFILL],
+            "decode_steps": n_steps[pa.STEP_DECODE], "sched_us_per_step": sched_s * 1e6 / steps,
+            "decode_gbps": kv_bytes / (dec_ms * 1e-3) / 1e9, "decode_kv_bytes": kv_bytes,
+            "decode_ms": dec_ms, "prefill_ms": pre_ms,
+            "prefill_tflops": pairs * FLOP_PER_PAIR / (pre_ms * 1e-3) / 1e12,
+            "tokens": int(sum(news)), "prompt_tokens": int(sum(prompts)),
+            "ms_per_step": wall * 1e3 / steps}
+
+
+def cpu_baseline_serve(budget_s: float) -> dict:
+    """The oracle scheduler over the same request stream, with the oracle's attention
+    (fp64, contiguous K/V) for the rows of its decode steps, one layer, until the budget
+    is spent."""
+    import oracle as O
+    from oracle import sched as S
+    from threadpoolctl import threadpool_limits
+
+    prompts, news = serve_stream()
+    max_blocks = -(-(1024 + 128 - 1) // SERVE_BS)
+    sc = S.Scheduler(SERVE_SLOTS, SERVE_BS, max_blocks, SERVE_CHUNK,
+                     S.Pool(int(SERVE_SLOTS * max_blocks * 1.1)))
+    for rid, (p, m) in enumerate(zip(prompts, news)):
+        sc.submit(rid, p, m)
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((1024 + 128, 8, 64))
+    v = rng.standard_normal((1024 + 128, 8, 64))
+    q = rng.standard_normal((1, 32, 64))
+    steps = rows = 0
+    sched_s = attn_s = 0.0
+    nbytes = 0
+    with threadpool_limits(limits=1):
+        while attn_s + sched_s < budget_s:
+            a = time.perf_counter()
+            plan = sc.step()
+            sched_s += time.perf_counter() - a
+            steps += 1
+            if plan.kind == S.IDLE and not sc.queue and not sc.active:
+                break
+            if plan.kind != S.DECODE:
+                continue
+            a = time.perf_counter()
+            for _, _, ctx, _, _ in plan.rows:
+                O.attention(q, k[:ctx], v[:ctx], [ctx], 0.125)
+                nbytes += ctx * KV_BYTES_PER_TOKEN
+                rows += 1
+            attn_s += time.perf_counter() - a
+    return {"value": nbytes / attn_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle scheduler over the first {steps} steps of the same stream "
+                      f"({sched_s * 1e6 / steps:.0f} us/step), fp64 oracle attention of the "
+                      f"{rows} rows of its decode steps, one layer ({nbytes / 1e9:.2f} GB of "
+                      f"KV) in {attn_s:.1f} s, 1 thread"}
+
+
+def main_serve(args) -> int:
+    cpu = None if args.no_cpu_baseline else cpu_baseline_serve(min(args.cpu_budget, 10.0))
+    res = run_serve()
+    line = {
+        "metric": METRIC, "value": round(res["decode_gbps"], 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": res["steps"], "warmup": 0, "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded request lengths; N(0,1) bf16 pools and rows)",
+        "config": {"workload": f"serve-{SERVE_REQS}req-{SERVE_SLOTS}slots-bs{SERVE_BS}",
+                   "layers": SERVE_LAYERS, "requests": SERVE_REQS, "slots": SERVE_SLOTS,
+                   "prefill_chunk": SERVE_CHUNK, "prompt_range": [128, 1024],
+                   "new_tokens_range": [16, 128], "block_size": SERVE_BS},
+        "roofline": {"bound": "hbm", "kernel": "pa_decode over the scheduled decode steps",
+                     "achieved": round(res["decode_gbps"], 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(res["decode_gbps"] / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_total": res["decode_kv_bytes"],
+                     "kernel_ms_total": round(res["decode_ms"], 3)},
+        "serve": {"steps": res["steps"], "prefill_steps": res["prefill_steps"],
+                  "decode_steps": res["decode_steps"],
+                  "sched_us_per_step": round(res["sched_us_per_step"], 2),
+                  "generated_tokens": res["tokens"], "prompt_tokens": res["prompt_tokens"],
+                  "wall_s": round(res["wall_s"], 3),
+                  "generated_tokens_per_s": round(res["tokens"] / res["wall_s"], 1),
+                  "prefill_tflops": round(res["prefill_tflops"], 1),
+                  "prefill_kernel_ms_total": round(res["prefill_ms"], 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
 
 
 def main_norm(args) -> int:
