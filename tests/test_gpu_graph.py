@@ -1,6 +1,8 @@
 """One step of the path (append, chunked prefill, split decode) captured in a HIP graph
 and replayed (marked ``gpu``): every replay, with eager work and synchronisations between
-replays, must reproduce the eager outputs and pools bit for bit."""
+replays, must reproduce the eager outputs and pools bit for bit.  Captured once in one
+stream and once with the prefill forked onto a second stream, concurrent with the decode,
+and joined back."""
 
 from __future__ import annotations
 
@@ -13,12 +15,14 @@ from tests.gpu_helpers import GpuCase, bits_host
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("overlap", [False, True])
+def test_graph_replays_match_eager(overlap):
     import torch
 
     import paged_kv_attention_31_amd as pa
 
-    print("[gpu-test] graph capture of append + prefill + decode", flush=True)
+    print(f"[gpu-test] graph capture of append + prefill + decode, overlap={overlap}",
+          flush=True)
     dec = GpuCase(W.custom_case([1, 700, 3000, 65, 129], [1] * 5, block_size=32, seed=95))
     pre = GpuCase(W.custom_case([600, 97], [200, 97], block_size=32, kind="prefill", seed=96))
     cd, cp = dec.case, pre.case
@@ -33,15 +37,22 @@ def test_graph_replays_match_eager():
     out_d = torch.empty((n_dec, 32, 64), dtype=torch.bfloat16, device="cuda:0")
     out_p = torch.empty((n_q, 32, 64), dtype=torch.bfloat16, device="cuda:0")
 
-    def step(stream):
+    side = torch.cuda.Stream()
+
+    def step(stream, fork=False):
         pa.kv_append(dec.geom, dec.k_new, dec.v_new, dec.kp, dec.vp, dec.bt, dec.cu_new, dec.ctx,
                      stream=stream)
         pa.kv_append(pre.geom, pre.k_new, pre.v_new, pre.kp, pre.vp, pre.bt, pre.cu_new, pre.ctx,
                      stream=stream)
+        if fork:
+            side.wait_stream(stream)
         pa.prefill(pre.geom, out_p, pre.q_pre, pre.kp, pre.vp, pre.pre_bt, pre.cu_q, pre.pre_ctx,
-                   max_q, mc_pre, cp.scale, kv_splits=4, workspace=ws_p, stream=stream)
+                   max_q, mc_pre, cp.scale, kv_splits=4, workspace=ws_p,
+                   stream=side if fork else stream)
         pa.decode(dec.geom, out_d, dec.q_dec, dec.kp, dec.vp, dec.dec_bt, dec.dec_ctx, mc_dec,
                   cd.scale, partition_tokens=part, workspace=ws_d, stream=stream)
+        if fork:
+            stream.wait_stream(side)
 
     step(torch.cuda.current_stream())
     torch.cuda.synchronize()
@@ -50,7 +61,7 @@ def test_graph_replays_match_eager():
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.graph(graph, stream=cap):
-        step(cap)
+        step(cap, fork=overlap)
     torch.cuda.synchronize()
     scratch = torch.zeros(1 << 20, device="cuda:0")
     for rep in range(4):
