@@ -56,7 +56,7 @@ int32_t blocks_for(int64_t tokens, int32_t bs) { return (int32_t)((tokens + bs -
 }  // namespace
 
 struct pa_sched {
-  std::mutex mu;
+  mutable std::mutex mu;
   pa_pool_t* pool = nullptr;
   int32_t num_slots = 0, bs = 0, max_blocks = 0, chunk = 0;
   std::deque<SchedReq> queue;       // submission order
@@ -135,9 +135,8 @@ int pa_sched_finish(pa_sched_t* s, int64_t req_id) {
 
 int32_t pa_sched_pending(const pa_sched_t* s) {
   if (!s) return -1;
-  auto* m = const_cast<pa_sched_t*>(s);
-  std::lock_guard<std::mutex> lock(m->mu);
-  return (int32_t)(m->queue.size() + m->active.size());
+  std::lock_guard<std::mutex> lock(s->mu);
+  return (int32_t)(s->queue.size() + s->active.size());
 }
 
 int pa_sched_step(pa_sched_t* s, pa_sched_step_t* info, int64_t* req_ids, int32_t* slots,
