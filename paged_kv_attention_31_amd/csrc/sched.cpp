@@ -212,7 +212,10 @@ int pa_sched_step(pa_sched_t* s, pa_sched_step_t* info, int64_t* req_ids, int32_
     const SchedReq& r = s->active[rows[k]];
     need += blocks_for((int64_t)r.cached + n_new[k], s->bs) - (int32_t)r.pages.size();
   }
-  if (need > pa_pool_num_free(s->pool)) {
+  // One pool call takes every page of the step (all or nothing, also against other users of
+  // the pool), in the order the rows then consume them.
+  std::vector<int32_t> fresh((size_t)need);
+  if (need > 0 && pa_pool_alloc(s->pool, (int32_t)need, fresh.data()) != PA_OK) {
     // only possible when pages promised to admitted requests were taken from the pool by
     // another user of it: nothing is scheduled
     s->last_kind = PA_STEP_IDLE;
@@ -220,16 +223,13 @@ int pa_sched_step(pa_sched_t* s, pa_sched_step_t* info, int64_t* req_ids, int32_
   }
 
   int32_t total_new = 0, max_ctx = 0, max_new = 0;
+  size_t next_page = 0;
   cu_new_lens[0] = 0;
   for (size_t k = 0; k < rows.size(); ++k) {
     SchedReq& r = s->active[rows[k]];
     const int32_t n = n_new[k];
     const int32_t grow = blocks_for((int64_t)r.cached + n, s->bs) - (int32_t)r.pages.size();
-    if (grow > 0) {
-      const size_t old = r.pages.size();
-      r.pages.resize(old + grow);
-      pa_pool_alloc(s->pool, grow, r.pages.data() + old);  // cannot fail: checked above
-    }
+    for (int32_t i = 0; i < grow; ++i) r.pages.push_back(fresh[next_page++]);
     r.cached += n;
     if (kind == PA_STEP_PREFILL) {
       if (r.cached == r.prompt) r.generated = 1;
