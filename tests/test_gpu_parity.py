@@ -347,3 +347,41 @@ def test_mixed_step_layer_sampled():
         ref = O.attention(O.bf16_to_f64(case.q_decode[d:d + 1]), O.bf16_to_f64(kl),
                           O.bf16_to_f64(vl), [int(case.ctx_lens[d])], case.scale)
         assert_close(dec[d:d + 1], ref, f"mixed decode seq {d}")
+
+
+def test_decode_workspace_needs_no_initialisation():
+    """The split-K workspace is scratch: whatever it holds before a call (random bytes, all
+    ones, the state another call with other shapes left), and however often it is reused,
+    the output is the clean run's, bit for bit."""
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    _announce("decode workspace contents")
+    case = W.custom_case([700, 1, 3000, 65, 129, 2049], [1] * 6, block_size=32, seed=97)
+    other = W.custom_case([5000, 17, 900], [1] * 3, block_size=32, seed=98)
+    g, go = GpuCase(case), GpuCase(other)
+    c, co = g.case, go.case
+    part = 128
+    mc, mco = int(c.ctx_lens.max()), int(co.ctx_lens.max())
+    nb = max(pa.decode_workspace_bytes(g.geom, len(c.decode_seqs), mc, part),
+             pa.decode_workspace_bytes(go.geom, len(co.decode_seqs), mco, part))
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda:0")
+
+    def run(gc, mctx):
+        out = torch.empty((len(gc.case.decode_seqs), 32, 64), dtype=torch.bfloat16,
+                          device="cuda:0")
+        pa.decode(gc.geom, out, gc.q_dec, gc.kp, gc.vp, gc.dec_bt, gc.dec_ctx, mctx,
+                  gc.case.scale, partition_tokens=part, workspace=ws)
+        return bits_host(out)
+
+    ref = bits_host(g.decode(partition_tokens=part))  # its own fresh workspace
+    ref_o = bits_host(go.decode(partition_tokens=part))
+    assert np.array_equal(run(g, mc), ref)
+    ws.copy_(torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda:0"))
+    assert np.array_equal(run(g, mc), ref)
+    ws.fill_(255)
+    assert np.array_equal(run(g, mc), ref)
+    for _ in range(3):  # alternating shapes on one workspace
+        assert np.array_equal(run(go, mco), ref_o)
+        assert np.array_equal(run(g, mc), ref)
