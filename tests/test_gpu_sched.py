@@ -2,7 +2,9 @@
 pa_sched_step goes, as is, to pa_kv_append and then pa_prefill or pa_decode; every output
 row must match the oracle's attention over the request's own tokens, taken contiguously
 from the generator (not from the pages), so a wrong block table, position or context
-length in a plan shows up as a wrong row.
+length in a plan shows up as a wrong row.  One run appends through pa_rope_kv_append
+instead: then Q and every cached K are turned by their positions (oracle: the rotation in
+fp64, rounded once to bf16), so the plans' positions are checked as well.
 
 Tolerance: the benchmark spec's mean-abs bar (1e-3) over the run, and per element the max-abs
 bar widened by one bf16 rounding of the result, |gpu - oracle| <= 1e-2 + 2^-8 |oracle|.
@@ -30,13 +32,14 @@ def _announce(msg):
     print(f"[gpu-test] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("bs,slots,chunk", [(16, 4, 96), (32, 6, 200)])
-def test_scheduler_plans_drive_the_kernels(bs, slots, chunk):
+@pytest.mark.parametrize("bs,slots,chunk,rope", [(16, 4, 96, False), (32, 6, 200, False),
+                                                  (16, 5, 128, True)])
+def test_scheduler_plans_drive_the_kernels(bs, slots, chunk, rope):
     import torch
 
     import paged_kv_attention_31_amd as pa
 
-    _announce(f"scheduler-driven run bs={bs} slots={slots} chunk={chunk}")
+    _announce(f"scheduler-driven run bs={bs} slots={slots} chunk={chunk} rope={rope}")
     rng = np.random.default_rng([92, bs])
     n_req, max_blocks, num_pages = 12, 24, 90
     reqs = {}
@@ -48,6 +51,15 @@ def test_scheduler_plans_drive_the_kernels(bs, slots, chunk):
             q=W.normal_bf16([92, bs, rid, 0], L * HQ * D).reshape(L, HQ, D),
             k=W.normal_bf16([92, bs, rid, 1], L * HKV * D).reshape(L, HKV, D),
             v=W.normal_bf16([92, bs, rid, 2], L * HKV * D).reshape(L, HKV, D))
+        if rope:  # what the kernel attends with: rows turned by position, in bf16
+            f = O.rope_freqs(D, 500000.0)
+            pos = np.arange(L)
+            for name in ("q", "k"):
+                r = reqs[rid]
+                r[name + "_att"] = O.f64_to_bf16(O.rotate(O.bf16_to_f64(r[name]),
+                                                          pos[:, None], f))
+        else:
+            reqs[rid]["q_att"], reqs[rid]["k_att"] = reqs[rid]["q"], reqs[rid]["k"]
     geom = pa.Geometry(num_pages, bs, HQ, HKV, D)
     e = bs * HKV * D
     kp = torch.full((num_pages, e), W.SENTINEL_BITS, dtype=torch.int16, device="cuda:0").view(
@@ -77,15 +89,19 @@ def test_scheduler_plans_drive_the_kernels(bs, slots, chunk):
             ks.append(r["k"][pos])
             vs.append(r["v"][pos])
             qs.append(r["q"][pos])
-            refs.append(O.attention(O.bf16_to_f64(r["q"][pos]), O.bf16_to_f64(r["k"][:ctx]),
+            refs.append(O.attention(O.bf16_to_f64(r["q_att"][pos]),
+                                    O.bf16_to_f64(r["k_att"][:ctx]),
                                     O.bf16_to_f64(r["v"][:ctx]), pos + 1, SCALE))
             if plan.kind == pa.STEP_DECODE or ctx == r["prompt"]:
                 produced[rid] += 1
         bt, ctx_d, cu = (i32_dev(plan.block_tables), i32_dev(plan.ctx_lens),
                          i32_dev(plan.cu_new_lens))
         qd = bf16_dev(np.concatenate(qs))
-        pa.kv_append(geom, bf16_dev(np.concatenate(ks)), bf16_dev(np.concatenate(vs)), kp, vp,
-                     bt, cu, ctx_d)
+        kd, vd = bf16_dev(np.concatenate(ks)), bf16_dev(np.concatenate(vs))
+        if rope:
+            pa.rope_kv_append(geom, qd, qd, kd, vd, kp, vp, bt, cu, ctx_d, rope_theta=500000.0)
+        else:
+            pa.kv_append(geom, kd, vd, kp, vp, bt, cu, ctx_d)
         out = torch.empty_like(qd)
         if plan.kind == pa.STEP_PREFILL:
             pa.prefill(geom, out, qd, kp, vp, bt, cu, ctx_d, max_q_len=plan.max_new_len,
