@@ -6,7 +6,7 @@ length in a plan shows up as a wrong row.  One run appends through pa_rope_kv_ap
 instead: then Q and every cached K are turned by their positions (oracle: the rotation in
 fp64, rounded once to bf16), so the plans' positions are checked as well.
 
-Tolerance: the benchmark spec's mean-abs bar (1e-3) over the run, and per element the max-abs
+Tolerance: the parity bar's mean-abs (1e-3) over the run, and per element its max-abs
 bar widened by one bf16 rounding of the result, |gpu - oracle| <= 1e-2 + 2^-8 |oracle|.
 The widening matters only for rows that see a handful of keys (the first rows of every
 prompt; here prompts start at 1 token), whose outputs are single V values of size up to
