@@ -148,6 +148,8 @@ int32_t pa_pool_refcount(const pa_pool_t* p, int32_t id);
  *                  cu_new_lens[n_seqs] = n_new_tokens
  *   ctx_lens       int32 [n_seqs] (device), lengths after the append
  * No two rows of one call may target the same slot.  n_new_tokens == 0 is a no-op.
+ * PA_ERR_INVALID_ARG for a missing pointer, n_seqs == 0 with rows to append, or
+ * n_new_tokens * num_kv_heads above 2^31 - 5.
  * ------------------------------------------------------------------------------- */
 int pa_kv_append(pa_geom_t g, const void* k_new, const void* v_new, void* k_pool,
                  void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -217,7 +219,8 @@ int pa_silu_mul(const void* gate, const void* up, int64_t ld_in, void* out, int6
  *   inv_freq        NULL or head_dim/2 fp32 frequencies (device)
  * A row whose position falls outside its block-table row, or whose page id is out of
  * range, is not appended (its Q is still rotated).  PA_ERR_INVALID_ARG for a missing
- * pointer, exactly one of q / q_out NULL, or a bad rope_theta without inv_freq.
+ * pointer, exactly one of q / q_out NULL, a bad rope_theta without inv_freq, or sizes
+ * as for pa_kv_append.
  * ------------------------------------------------------------------------------- */
 int pa_rope_kv_append(pa_geom_t g, const void* q, void* q_out, const void* k_new,
                       const void* v_new, void* k_pool, void* v_pool,

@@ -260,6 +260,7 @@ int pa_rope_kv_append(pa_geom_t g, const void* q, void* q_out, const void* k_new
   if (n_seqs == 0) return PA_ERR_INVALID_ARG;
   if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !cu_new_lens || !ctx_lens)
     return PA_ERR_INVALID_ARG;
+  if ((int64_t)n_new_tokens * g.num_kv_heads > (int64_t)INT32_MAX - 4) return PA_ERR_INVALID_ARG;
   return hip_status(pa::launch_rope_kv_append(
       to_launch(g), q, q_out, k_new, v_new, k_pool, v_pool, block_tables, max_blocks_per_seq,
       cu_new_lens, ctx_lens, n_seqs, n_new_tokens, rope_theta, inv_freq,
