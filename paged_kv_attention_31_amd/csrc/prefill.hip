@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
       softmax(s0, k0, p0);
       pv(v0o, p0);
     }
-    {
+    if (__builtin_expect(k0 + 32 < kend, 1)) {  // else masked whole: nothing to add
       VOps v1o;
       read_v(buf, 1, v1o);
       softmax(s1, k0 + 32, p1);
