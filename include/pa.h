@@ -271,6 +271,26 @@ int pa_decode(pa_geom_t g, void* out, const void* q, const void* k_pool, const v
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * decode_append: the decode step's append and attention in one launch ([guide]
+ * §推理流程：从Prefill到Decode: each decode step appends one token's K/V, then attends).
+ * Row s of k_new / v_new ([n_seqs][num_kv_heads][head_dim] bf16, device) is the K/V of
+ * position ctx_lens[s] - 1 of sequence s (ctx_lens counts it, as for pa_decode).  It is
+ * written into the pools at that position, exactly as pa_kv_append with one row per
+ * sequence would write it (not written if the page id is out of range; nothing for
+ * ctx_lens[s] = 0), and the query attends over all ctx_lens[s] tokens, the new one
+ * included.  Outputs and pools equal, bit for bit, those of pa_kv_append
+ * (cu_new_lens = 0, 1, ..., n_seqs) followed by pa_decode with the same arguments.
+ * Every other argument, the workspace and the errors are as for pa_decode; k_pool /
+ * v_pool are written.  ctx_lens[s] must not exceed max_ctx_len.
+ * ------------------------------------------------------------------------------- */
+int pa_decode_append(pa_geom_t g, void* out, const void* q, const void* k_new,
+                     const void* v_new, void* k_pool, void* v_pool,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* ctx_lens, int32_t n_seqs, int32_t max_ctx_len, float scale,
+                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Prefill, whole prompts or chunks ([guide] §推理流程: prefill handles every prompt
  * token in parallel; [实战] §算子融合: tiled attention with online softmax never
  * materialises the seq x seq score matrix).  Query rows are packed by sequence: rows

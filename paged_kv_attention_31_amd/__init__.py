@@ -26,7 +26,8 @@ __all__ = [
     "PagedAttnError", "Geometry", "PagePool", "Scheduler", "StepPlan", "STEP_IDLE",
     "STEP_PREFILL", "STEP_DECODE", "page_bytes", "kv_append", "rope_kv_append",
     "copy_pages", "residual_rmsnorm", "silu_mul",
-    "decode_partition_tokens", "decode_workspace_bytes", "decode", "prefill_workspace_bytes",
+    "decode_partition_tokens", "decode_workspace_bytes", "decode", "decode_append",
+    "prefill_workspace_bytes",
     "prefill", "library",
 ]
 
@@ -380,6 +381,39 @@ def decode(geom: Geometry, out, q, k_pool, v_pool, block_tables, ctx_lens, max_c
                                int(max_ctx_len), float(scale), int(partition_tokens),
                                _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_decode")
+
+
+def decode_append(geom: Geometry, out, q, k_new, v_new, k_pool, v_pool, block_tables, ctx_lens,
+                  max_ctx_len: int, scale: float, partition_tokens: int = 0, workspace=None,
+                  stream=None) -> None:
+    """One decode step in one launch (see pa_decode_append): row s of ``k_new`` /
+    ``v_new`` [n_seqs, Hkv, d] is appended at position ctx_lens[s] - 1, then the query row
+    attends over the whole context.  ``workspace`` as for :func:`decode`."""
+    import torch
+
+    n = int(ctx_lens.numel())
+    rows = n * geom.num_q_heads * geom.head_dim
+    _dev(out, "out", torch.bfloat16, rows)
+    _dev(q, "q", torch.bfloat16, rows)
+    for name, x in (("k_new", k_new), ("v_new", v_new)):
+        _dev(x, name, torch.bfloat16, n * geom.num_kv_heads * geom.head_dim)
+    for name, x in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(x, name, torch.bfloat16, geom.num_pages * geom.page_elems)
+    _dev(block_tables, "block_tables", torch.int32, dims=2)
+    _dev(ctx_lens, "ctx_lens", torch.int32, n)
+    _need(block_tables.shape[0] == n, "block_tables rows != n_seqs")
+    need = decode_workspace_bytes(geom, n, int(max_ctx_len), int(partition_tokens))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
+    st = _lib.load().pa_decode_append(
+        geom.c(), _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(ctx_lens), n, int(max_ctx_len),
+        float(scale), int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "pa_decode_append")
 
 
 def prefill_workspace_bytes(geom: Geometry, n_seqs: int, max_q_len: int, max_ctx_len: int,

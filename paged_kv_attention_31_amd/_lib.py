@@ -80,6 +80,9 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [PaGeom, _c_i32, _c_i32, _c_i32]),
     "pa_decode": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32,
                                  _c_i32, ctypes.c_float, _c_i32, _c_p, ctypes.c_size_t, _c_p]),
+    "pa_decode_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                        _c_i32, _c_p, _c_i32, _c_i32, ctypes.c_float, _c_i32,
+                                        _c_p, ctypes.c_size_t, _c_p]),
     "pa_prefill_workspace_bytes": (ctypes.c_size_t, [PaGeom, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_prefill": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p,
                                   _c_i32, _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_i32, _c_p,

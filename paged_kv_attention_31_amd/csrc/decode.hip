@@ -80,15 +80,25 @@ struct DecodeTile {
   static constexpr int NV = BS / 8;       // 16-byte V loads per page (= dims per lane)
   uint4 k[8];
   uint4 v[PPT][NV];
+  int new_page;  // APPEND: page of the sequence's newest token if this tile holds it, else -1
 };
 
-template <int BS>
+// APPEND: one new token per sequence (the one at ctx_lens[s] - 1, rows k_new / v_new
+// [n_seqs][Hkv][64]) joins the cache in the same launch.  The wave that streams the
+// segment's last tile takes the token's K/V from those rows (they come in through lanes
+// 32..47 of the q load, so no load is added) in place of the pool slot, and writes them
+// into the slot with two buffer stores that every tile issues and whose range is empty
+// unless the tile holds the new token (equal store counts on every path, as for the result
+// stores).  No other wave reads that slot: a (page, KV head) slice belongs to one tile.
+template <int BS, bool APPEND>
 __global__ __launch_bounds__(256) void decode_stream_kernel(
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
     int2* __restrict__ ws_desc, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
     int max_blocks, const int32_t* __restrict__ ctx_lens, int n_seqs, int ctx_cap,
-    int num_pages, int num_kv_heads, int n_workers, float qk_scale) {
+    int num_pages, int num_kv_heads, int n_workers, float qk_scale,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* k_dst,
+    uint16_t* v_dst) {
   using Tile = DecodeTile<BS>;
   constexpr int PPT = Tile::PPT;
   constexpr int NV = Tile::NV;
@@ -109,6 +119,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t p_sh[kDecodeWaves][kGroup][64];
   __shared__ __attribute__((aligned(16))) float fin_sh[kDecodeWaves][kGroup * kHeadDim];
   __shared__ float2 fin_ml[kDecodeWaves][kGroup];
+  __shared__ uint4 kvn_sh[kDecodeWaves][2][16];  // APPEND: new K (8 pieces), then V (8 pieces)
 
   // ---- 1. tiles per sequence and their exclusive prefix sum over 256 chunks -----------
   const int chunk = (n_seqs + 255) / 256;
@@ -212,12 +223,25 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     return block_tables[(size_t)c.s * max_blocks + blk];
   };
   // q of the tile's segment: lane l (and l + 32) reads piece l % 8 of head (l % 32) / 8
+  // (APPEND: lanes 32..39 read the segment's new K row, lanes 40..47 its new V row, 16 bytes
+  // each; lanes 48..63 repeat the K row)
   auto load_q = [&](const Cursor& c) -> uint4 {
-    return reinterpret_cast<const uint4*>(q + ((size_t)c.s * hq + c.g * kGroup) * kHeadDim)
-        [lane & 31];
+    if constexpr (APPEND) {
+      const uint16_t* src =
+          lane < 32 ? q + ((size_t)c.s * hq + c.g * kGroup) * kHeadDim + 8 * lane
+                    : ((lane >> 3) == 5 ? v_new : k_new) + ((size_t)c.s * hkv + c.g) * kHeadDim +
+                          8 * (lane & 7);
+      return *reinterpret_cast<const uint4*>(src);
+    } else {
+      return reinterpret_cast<const uint4*>(q + ((size_t)c.s * hq + c.g * kGroup) * kHeadDim)
+          [lane & 31];
+    }
   };
   auto store_q = [&](int slot, uint4 v) {
     if (lane < 32) q_sh[w][slot][lane >> 3][lane & 7] = v;
+    if constexpr (APPEND) {
+      if (lane >= 32 && lane < 48) kvn_sh[w][slot][lane - 32] = v;
+    }
   };
   // Issue the K/V loads of a tile.  `live` false (a tile past the end of the range)
   // points every lane at one 16-byte piece, so each load instruction fetches one line.
@@ -232,6 +256,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       if ((unsigned)pg[j] >= (unsigned)num_pages) {
         bad = true;
         pg[j] = 0;
+      }
+    }
+    if constexpr (APPEND) {
+      t.new_page = -1;
+      if (live && c.ctx > 0 && c.i == c.nt - 1) {
+        const int pgn = readlane_i(pid, ((c.ctx - 1) % kTile) / BS);
+        if ((unsigned)pgn < (unsigned)num_pages) t.new_page = pgn;
       }
     }
     int kpage = pg[0];
@@ -264,8 +295,39 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   reset();
 
   // scores, online-softmax update and P.V of the tile at cursor c, held in t
-  auto compute = [&](const Tile& t, const Cursor& c, int slot) {
+  auto compute = [&](Tile& t, const Cursor& c, int slot) {
     const int nvalid = min(max(c.ctx - c.i * kTile, 0), kTile);
+    if constexpr (APPEND) {
+      if (c.ctx > 0 && c.i == c.nt - 1) {  // uniform: the tile holds the newest token
+        const int pn = nvalid - 1;           // its index in the tile
+        if (lane == pn) {
+#pragma unroll
+          for (int p = 0; p < 8; ++p) t.k[p] = kvn_sh[w][slot][p];
+        }
+        // V: the lanes whose 8-token run holds the token replace its element
+        const int pin = pn % BS;
+        const int jn = pn / BS;
+        const int e = pin & 7;
+        if (lane % LPR == pin / 8) {
+          const uint16_t* vn = reinterpret_cast<const uint16_t*>(&kvn_sh[w][slot][8]);
+#pragma unroll
+          for (int j = 0; j < PPT; ++j) {
+            if (j != jn) continue;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+              const uint32_t x = vn[lane / LPR + i * RPI];
+              const uint32_t lo_mask = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+              const uint32_t ins = (e & 1) ? (x << 16) : x;
+              const int wd = e >> 1;
+              t.v[j][i].x = wd == 0 ? ((t.v[j][i].x & lo_mask) | ins) : t.v[j][i].x;
+              t.v[j][i].y = wd == 1 ? ((t.v[j][i].y & lo_mask) | ins) : t.v[j][i].y;
+              t.v[j][i].z = wd == 2 ? ((t.v[j][i].z & lo_mask) | ins) : t.v[j][i].z;
+              t.v[j][i].w = wd == 3 ? ((t.v[j][i].w & lo_mask) | ins) : t.v[j][i].w;
+            }
+          }
+        }
+      }
+    }
     // q comes from LDS as 16-byte broadcasts, two pieces (4 heads each) in registers at a
     // time: the reads of piece p + 2 are tied (through an empty asm) to the dot products
     // of piece p, so the compiler can neither hoist all 32 reads (128 registers) nor
@@ -494,6 +556,23 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     bad_nxt = load_kv(nxt, c1, pid_n1, t + 1 < L);
     seg_bad |= bad_cur;
     compute(cur, cc, t & 1);
+    if constexpr (APPEND) {
+      // the new token's K row (lanes 0..7, one 16-byte piece each) and V column (lane d,
+      // dimension d) into its pool slot; an empty range unless this tile holds the token
+      const bool has = cur.new_page >= 0;
+      const int pin = has ? (cc.ctx - 1) % BS : 0;
+      const int nrec = has ? (int)(head_stride * 2) : 0;
+      const size_t base = has ? (size_t)cur.new_page * page_stride + (size_t)cc.g * head_stride : 0;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          k_dst + base, 0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          v_dst + base, 0, nrec, kRsrcWord3);
+      const uint4 kp = kvn_sh[w][t & 1][lane & 7];
+      const uint16_t vd = reinterpret_cast<const uint16_t*>(&kvn_sh[w][t & 1][8])[lane];
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{kp.x, kp.y, kp.z, kp.w}, rk,
+                                             lane < 8 ? (lane * BS + pin) * 16 : nrec, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(vd, rv, (lane * BS + pin) * 2, 0, 0);
+    }
     const bool ends = t == L - 1 || cc.i == cc.nt - 1;
     __amdgpu_buffer_rsrc_t r_data = rsrc_none(), r_ml = rsrc_none();
     if (ends) finish(cc, seg_whole, seg_whole && cc.i == cc.nt - 1, seg_bad, r_data, r_ml);
@@ -627,7 +706,8 @@ DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partit
 hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* out, const void* q,
                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
                          int max_blocks, const int32_t* ctx_lens, int n_seqs, int max_ctx_len,
-                         float scale, void* workspace, hipStream_t stream) {
+                         float scale, void* workspace, hipStream_t stream, const void* k_new,
+                         const void* v_new) {
   const float qk_scale = scale * kLog2e;
   float* ws_o = nullptr;
   float2* ws_ml = nullptr;
@@ -646,15 +726,21 @@ hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* ou
   auto* qq = static_cast<const uint16_t*>(q);
   auto* kp = static_cast<const uint16_t*>(k_pool);
   auto* vp = static_cast<const uint16_t*>(v_pool);
+  auto* kn = static_cast<const uint16_t*>(k_new);
+  auto* vn = static_cast<const uint16_t*>(v_new);
+  auto* kd = const_cast<uint16_t*>(kp);  // written only by the appending variant
+  auto* vd = const_cast<uint16_t*>(vp);
+#define PA_DECODE_LAUNCH(B, A)                                                                  \
+  hipLaunchKernelGGL((decode_stream_kernel<B, A>), grid, block, 0, stream, o, ws_o, ws_ml,      \
+                     ws_desc, qq, kp, vp, block_tables, max_blocks, ctx_lens, n_seqs, ctx_cap,  \
+                     geo.num_pages, geo.num_kv_heads, workers, qk_scale, kn, vn, kd, vd)
+  const bool append = k_new != nullptr;
   if (geo.block_size == 16) {
-    hipLaunchKernelGGL(decode_stream_kernel<16>, grid, block, 0, stream, o, ws_o, ws_ml, ws_desc,
-                       qq, kp, vp, block_tables, max_blocks, ctx_lens, n_seqs, ctx_cap,
-                       geo.num_pages, geo.num_kv_heads, workers, qk_scale);
+    if (append) PA_DECODE_LAUNCH(16, true); else PA_DECODE_LAUNCH(16, false);
   } else {
-    hipLaunchKernelGGL(decode_stream_kernel<32>, grid, block, 0, stream, o, ws_o, ws_ml, ws_desc,
-                       qq, kp, vp, block_tables, max_blocks, ctx_lens, n_seqs, ctx_cap,
-                       geo.num_pages, geo.num_kv_heads, workers, qk_scale);
+    if (append) PA_DECODE_LAUNCH(32, true); else PA_DECODE_LAUNCH(32, false);
   }
+#undef PA_DECODE_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !plan.merge) return e;
   hipLaunchKernelGGL(decode_merge_kernel, grid, block, 0, stream, o, ws_o, ws_ml, ws_desc, workers,

@@ -71,7 +71,8 @@ DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partit
 hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* out, const void* q,
                          const void* k_pool, const void* v_pool, const int32_t* block_tables,
                          int max_blocks, const int32_t* ctx_lens, int n_seqs, int max_ctx_len,
-                         float scale, void* workspace, hipStream_t stream);
+                         float scale, void* workspace, hipStream_t stream,
+                         const void* k_new = nullptr, const void* v_new = nullptr);
 
 // Prefill: one workgroup per (query tile of 32, sequence, KV head); when that gives fewer
 // than two workgroups per compute unit the tile's keys are split into up to

@@ -1,0 +1,95 @@
+"""pa_decode_append (marked ``gpu``): the decode step's append and attention in one launch
+must give, bit for bit, the outputs and pools of pa_kv_append (one row per sequence)
+followed by pa_decode, and match the oracle within the parity bar."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.gpu_helpers import (assert_close, bf16_dev, bits_host, geometry, i32_dev,
+                               sentinel_pools)
+from tests.helpers import oracle_decode, oracle_pools
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _both_paths(case, part, ctx_override=None, bt_override=None):
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    geom = geometry(case)
+    hkv, d = case.num_kv_heads, case.head_dim
+    kp, vp = sentinel_pools(case)
+    bt = i32_dev(case.block_tables if bt_override is None else bt_override)
+    if case.k_setup.shape[0]:
+        pa.kv_append(geom, bf16_dev(case.k_setup), bf16_dev(case.v_setup), kp, vp, bt,
+                     i32_dev(case.cu_setup_lens), i32_dev(case.setup_ctx_lens))
+    ctx_h = case.ctx_lens if ctx_override is None else ctx_override
+    ctx = i32_dev(ctx_h)
+    n = case.n_seqs
+    k_new = bf16_dev(case.k_new.reshape(n, hkv, d))
+    v_new = bf16_dev(case.v_new.reshape(n, hkv, d))
+    q = bf16_dev(case.q_decode)
+    mc = int(max(int(ctx_h.max()), 1))
+    ka, va, kb, vb = kp.clone(), vp.clone(), kp.clone(), vp.clone()
+    out_a = torch.empty((n, 32, 64), dtype=torch.bfloat16, device="cuda:0")
+    out_b = torch.empty_like(out_a)
+    pa.kv_append(geom, k_new, v_new, ka, va, bt, i32_dev(np.arange(n + 1, dtype=np.int32)),
+                 ctx)
+    pa.decode(geom, out_a, q, ka, va, bt, ctx, mc, case.scale, partition_tokens=part)
+    pa.decode_append(geom, out_b, q, k_new, v_new, kb, vb, bt, ctx, mc, case.scale,
+                     partition_tokens=part)
+    torch.cuda.synchronize()
+    same_pools = bool(torch.equal(ka.view(torch.int16), kb.view(torch.int16)) and
+                      torch.equal(va.view(torch.int16), vb.view(torch.int16)))
+    return bits_host(out_a), bits_host(out_b), same_pools, out_b, (kb, vb)
+
+
+@pytest.mark.parametrize("wl", [1, 2])
+def test_decode_append_workloads(wl):
+    case = W.make_case(wl)
+    _announce(f"decode_append workload {wl}")
+    a, b, same, out_b, _ = _both_paths(case, 0)
+    assert np.array_equal(a, b) and same
+    kp_o, vp_o = oracle_pools(case)
+    assert_close(out_b, oracle_decode(case, kp_o, vp_o), f"workload {wl}")
+
+
+@pytest.mark.parametrize("bs,part", [(16, 0), (16, 128), (32, 0), (32, 64), (32, 256)])
+def test_decode_append_lengths_and_cuts(bs, part):
+    ctx = [1, 2, 63, 64, 65, 700, 3000, 2049, 128, 33, 16, 17]
+    case = W.custom_case(ctx, [1] * len(ctx), block_size=bs, seed=99 + bs)
+    _announce(f"decode_append bs={bs} partition={part}")
+    a, b, same, out_b, _ = _both_paths(case, part)
+    assert np.array_equal(a, b) and same
+    kp_o, vp_o = oracle_pools(case)
+    assert_close(out_b, oracle_decode(case, kp_o, vp_o), f"bs {bs} partition {part}")
+
+
+def test_decode_append_empty_context_and_bad_page():
+    ctx = [40, 300, 7, 129]
+    case = W.custom_case(ctx, [1] * 4, block_size=16, seed=101)
+    _announce("decode_append empty context and out-of-range page")
+    c0 = case.ctx_lens.copy()
+    c0[2] = 0  # no token: nothing appended, a zero row
+    bt = case.block_tables.copy()
+    bt[1, (int(c0[1]) - 1) // 16] = case.num_pages + 3  # the new token's page is invalid
+    a, b, same, out_b, _ = _both_paths(case, 64, ctx_override=c0, bt_override=bt)
+    assert np.array_equal(a, b) and same
+    host = out_b.float().cpu().numpy()
+    assert np.all(host[2] == 0)
+    assert np.all(np.isnan(host[1])) and np.all(np.isfinite(host[[0, 3]]))
+
+
+def test_decode_append_long_contexts_sampled():
+    case = W.make_case(4)
+    _announce("decode_append workload 4")
+    a, b, same, out_b, _ = _both_paths(case, 0)
+    assert np.array_equal(a, b) and same
