@@ -30,6 +30,11 @@ pa_copy_pages (the copy half of copy-on-write) on 4096 block-size-32 pages of bo
 ``value`` is the decode KV-read rate over the scheduled decode launches, with the
 scheduler's host time per step and the generated tokens per second of the whole loop.
 
+The pure decode workloads (decode-batched, decode-long) run their step as one
+pa_decode_append launch per layer (the one-token append fused into the decode); the step
+with pa_kv_append + pa_decode is timed beside it (``step_timing``) and ``roofline_decode_only``
+gives pa_decode alone.
+
 No timed launch finds its inputs in a cache: the decode-batched and prefill workloads (one
 layer each) walk through 6 and 16 independent copies of their layer, and the kernel-level
 workloads cycle back-to-back launches through independent buffer sets of at least 1 GiB
@@ -285,15 +290,64 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     def avg_ms(pairs):
         return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
 
+    # A pure decode step (one new token per sequence, no prefill) also runs as one
+    # pa_decode_append launch per layer: timed per launch (events) and as a graph, and
+    # that step gives the value.
+    fused = None
+    if n_dec and not n_pre and int(base.cu_new_lens[-1]) == n_dec:
+        hkv = base.num_kv_heads
+
+        def fused_step(st, ev=None):
+            for L in layers:
+                if ev is not None:
+                    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a0.record(st)
+                pa.decode_append(geom, out_dec, L.q_dec, L.k_new.view(n_dec, hkv, 64),
+                                 L.v_new.view(n_dec, hkv, 64), L.kp, L.vp, dec_bt, dec_ctx,
+                                 max_ctx_dec, scale, partition_tokens=part, workspace=ws,
+                                 stream=st)
+                if ev is not None:
+                    a1.record(st)
+                    ev.append((a0, a1))
+
+        ev_fused = []
+        for _ in range(warmup):
+            fused_step(stream)
+        for _ in range(steps):
+            fused_step(stream, ev_fused)
+        torch.cuda.synchronize()
+        graph_f = torch.cuda.CUDAGraph()
+        cap_f = torch.cuda.Stream()
+        cap_f.wait_stream(stream)
+        with torch.cuda.graph(graph_f, stream=cap_f):
+            fused_step(cap_f)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            graph_f.replay()
+        torch.cuda.synchronize()
+        log(f"timing {steps} graph replays of the fused step")
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph_f.replay()
+        torch.cuda.synchronize()
+        fused = {"ms_per_step": (time.perf_counter() - t0) * 1e3 / steps,
+                 "kernel_ms": avg_ms(ev_fused)}
+
     ms_step = wall * 1e3 / steps
     res = {"ms_per_step": ms_step, "ms_per_step_eager": wall_eager * 1e3 / steps,
-           "n_layers": n_layers, "partition_tokens": part, "append_ms": avg_ms(ev_app)}
+           "n_layers": n_layers, "partition_tokens": part, "append_ms": avg_ms(ev_app),
+           "fused": fused}
     kv_bytes_layer = base.kv_tokens() * KV_BYTES_PER_TOKEN
     if n_dec:
         dec_ms = avg_ms(ev_dec)
         res.update(decode_ms=dec_ms, decode_bytes_per_launch=kv_bytes_layer,
                    decode_gbps=kv_bytes_layer / (dec_ms * 1e-3) / 1e9,
                    value=kv_bytes_layer * n_layers / (ms_step * 1e-3) / 1e9, unit="GB/s")
+        if fused is not None:
+            fused.update(value=kv_bytes_layer * n_layers / (fused["ms_per_step"] * 1e-3) / 1e9,
+                         kernel_gbps=kv_bytes_layer / (fused["kernel_ms"] * 1e-3) / 1e9,
+                         separate_value=res["value"], separate_ms_per_step=ms_step)
+            res.update(value=fused["value"], ms_per_step=fused["ms_per_step"])
     if n_pre:
         pre_ms = avg_ms(ev_pre)
         flops = base.prefill_pairs() * FLOP_PER_PAIR
@@ -478,13 +532,30 @@ def main() -> int:
     }
     if "decode_ms" in res:
         ach = res["decode_gbps"]
-        line["roofline"] = {"bound": "hbm",
-                            "kernel": "pa_decode (decode_stream_kernel + decode_merge_kernel)",
-                            "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": round(ach / HBM_PEAK_GBPS, 4),
-                            "traffic": hbm_traffic(args.workload),
-                            "bytes_per_launch": res["decode_bytes_per_launch"],
-                            "avg_launch_ms": round(res["decode_ms"], 5)}
+        dec_line = {"bound": "hbm",
+                    "kernel": "pa_decode (decode_stream_kernel + decode_merge_kernel)",
+                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBPS, 4),
+                    "traffic": hbm_traffic(args.workload),
+                    "bytes_per_launch": res["decode_bytes_per_launch"],
+                    "avg_launch_ms": round(res["decode_ms"], 5)}
+        fz = res.get("fused")
+        if fz is not None:
+            # the step that value times: one pa_decode_append launch per layer
+            line["step_timing"].update(
+                fused_append=True, separate_append_graph_ms=round(fz["separate_ms_per_step"], 4),
+                separate_append_value=round(fz["separate_value"], 2))
+            ach = fz["kernel_gbps"]
+            line["roofline"] = {
+                "bound": "hbm",
+                "kernel": "pa_decode_append (decode_stream_kernel<bs, append> + decode_merge_kernel)",
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                "bytes_per_launch": res["decode_bytes_per_launch"],
+                "avg_launch_ms": round(fz["kernel_ms"], 5)}
+            line["roofline_decode_only"] = dec_line
+        else:
+            line["roofline"] = dec_line
     if "prefill_ms" in res:
         ach = res["prefill_tflops"]
         key = "roofline_prefill" if "roofline" in line else "roofline"

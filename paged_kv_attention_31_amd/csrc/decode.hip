@@ -567,10 +567,17 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
           k_dst + base, 0, nrec, kRsrcWord3);
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
           v_dst + base, 0, nrec, kRsrcWord3);
-      const uint4 kp = kvn_sh[w][t & 1][lane & 7];
-      const uint16_t vd = reinterpret_cast<const uint16_t*>(&kvn_sh[w][t & 1][8])[lane];
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{kp.x, kp.y, kp.z, kp.w}, rk,
-                                             lane < 8 ? (lane * BS + pin) * 16 : nrec, 0, 0);
+      // the row is read from LDS only on the tile that writes it (the stores themselves are
+      // issued on every tile)
+      u32x4_t kp = {0u, 0u, 0u, 0u};
+      uint16_t vd = 0;
+      if (__builtin_expect(has, 0)) {
+        const uint4 k4 = kvn_sh[w][t & 1][lane & 7];
+        kp = u32x4_t{k4.x, k4.y, k4.z, k4.w};
+        vd = reinterpret_cast<const uint16_t*>(&kvn_sh[w][t & 1][8])[lane];
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(kp, rk, lane < 8 ? (lane * BS + pin) * 16 : nrec, 0,
+                                             0);
       __builtin_amdgcn_raw_buffer_store_b16(vd, rv, (lane * BS + pin) * 2, 0, 0);
     }
     const bool ends = t == L - 1 || cc.i == cc.nt - 1;
