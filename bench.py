@@ -26,7 +26,8 @@ pa_copy_pages (the copy half of copy-on-write) on 4096 block-size-32 pages of bo
 (the prefill workload's tokens at the 1B MLP width) with pa_residual_rmsnorm of the
 [4622, 2048] hidden rows beside it.  ``--workload serve`` runs the slot scheduler
 (pa_sched_step) over 256 requests (prompts U[128, 1024], U[16, 128] new tokens, 64 slots,
-16 layers), each plan uploaded and run through pa_kv_append + pa_prefill / pa_decode;
+16 layers), each plan uploaded and run through pa_kv_append + pa_prefill, or
+pa_decode_append for decode steps;
 ``value`` is the decode KV-read rate over the scheduled decode launches, with the
 scheduler's host time per step and the generated tokens per second of the whole loop.
 
@@ -750,15 +751,16 @@ def run_serve() -> dict:
         ctx = torch.from_numpy(plan.ctx_lens).to(dev)
         cu = torch.from_numpy(plan.cu_new_lens).to(dev)
         for kp, vp in pools:  # one block table serves every layer
-            pa.kv_append(geom, k_src[:t], v_src[:t], kp, vp, bt, cu, ctx, stream=stream)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
             if plan.kind == pa.STEP_PREFILL:
+                pa.kv_append(geom, k_src[:t], v_src[:t], kp, vp, bt, cu, ctx, stream=stream)
+                e0.record(stream)
                 pa.prefill(geom, out[:t], q_src[:t], kp, vp, bt, cu, ctx, plan.max_new_len,
                            plan.max_ctx_len, 0.125, causal=True, stream=stream)
-            else:
-                pa.decode(geom, out[:n], q_src[:n], kp, vp, bt, ctx, plan.max_ctx_len, 0.125,
-                          stream=stream)
+            else:  # one new token per row: append and attend in one launch
+                e0.record(stream)
+                pa.decode_append(geom, out[:n], q_src[:n], k_src[:n], v_src[:n], kp, vp, bt,
+                                 ctx, plan.max_ctx_len, 0.125, stream=stream)
             e1.record(stream)
             ev[plan.kind].append((e0, e1))
         if plan.kind == pa.STEP_PREFILL:
@@ -840,7 +842,7 @@ def main_serve(args) -> int:
                    "layers": SERVE_LAYERS, "requests": SERVE_REQS, "slots": SERVE_SLOTS,
                    "prefill_chunk": SERVE_CHUNK, "prompt_range": [128, 1024],
                    "new_tokens_range": [16, 128], "block_size": SERVE_BS},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode over the scheduled decode steps",
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_append over the scheduled decode steps",
                      "achieved": round(res["decode_gbps"], 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(res["decode_gbps"] / HBM_PEAK_GBPS, 4),
                      "traffic": None, "bytes_total": res["decode_kv_bytes"],

@@ -2,7 +2,8 @@
 pa_sched_step goes, as is, to pa_kv_append and then pa_prefill or pa_decode; every output
 row must match the oracle's attention over the request's own tokens, taken contiguously
 from the generator (not from the pages), so a wrong block table, position or context
-length in a plan shows up as a wrong row.  One run appends through pa_rope_kv_append
+length in a plan shows up as a wrong row.  One run serves its decode steps with
+pa_decode_append (append and attention in one launch).  One run appends through pa_rope_kv_append
 instead: then Q and every cached K are turned by their positions (oracle: the rotation in
 fp64, rounded once to bf16), so the plans' positions are checked as well.
 
@@ -32,14 +33,16 @@ def _announce(msg):
     print(f"[gpu-test] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("bs,slots,chunk,rope", [(16, 4, 96, False), (32, 6, 200, False),
-                                                  (16, 5, 128, True)])
-def test_scheduler_plans_drive_the_kernels(bs, slots, chunk, rope):
+@pytest.mark.parametrize("bs,slots,chunk,rope,fused", [(16, 4, 96, False, False),
+                                                        (32, 6, 200, False, True),
+                                                        (16, 5, 128, True, False)])
+def test_scheduler_plans_drive_the_kernels(bs, slots, chunk, rope, fused):
     import torch
 
     import paged_kv_attention_31_amd as pa
 
-    _announce(f"scheduler-driven run bs={bs} slots={slots} chunk={chunk} rope={rope}")
+    _announce(f"scheduler-driven run bs={bs} slots={slots} chunk={chunk} rope={rope} "
+              f"fused={fused}")
     rng = np.random.default_rng([92, bs])
     n_req, max_blocks, num_pages = 12, 24, 90
     reqs = {}
@@ -98,17 +101,23 @@ def test_scheduler_plans_drive_the_kernels(bs, slots, chunk, rope):
                          i32_dev(plan.cu_new_lens))
         qd = bf16_dev(np.concatenate(qs))
         kd, vd = bf16_dev(np.concatenate(ks)), bf16_dev(np.concatenate(vs))
-        if rope:
-            pa.rope_kv_append(geom, qd, qd, kd, vd, kp, vp, bt, cu, ctx_d, rope_theta=500000.0)
-        else:
-            pa.kv_append(geom, kd, vd, kp, vp, bt, cu, ctx_d)
         out = torch.empty_like(qd)
-        if plan.kind == pa.STEP_PREFILL:
-            pa.prefill(geom, out, qd, kp, vp, bt, cu, ctx_d, max_q_len=plan.max_new_len,
-                       max_ctx_len=plan.max_ctx_len, scale=SCALE, causal=True)
+        if fused and plan.kind == pa.STEP_DECODE:  # append and attend in one launch
+            n = len(plan.req_ids)
+            pa.decode_append(geom, out, qd, kd.view(n, HKV, D), vd.view(n, HKV, D), kp, vp, bt,
+                             ctx_d, max_ctx_len=plan.max_ctx_len, scale=SCALE)
         else:
-            pa.decode(geom, out, qd, kp, vp, bt, ctx_d, max_ctx_len=plan.max_ctx_len,
-                      scale=SCALE)
+            if rope:
+                pa.rope_kv_append(geom, qd, qd, kd, vd, kp, vp, bt, cu, ctx_d,
+                                  rope_theta=500000.0)
+            else:
+                pa.kv_append(geom, kd, vd, kp, vp, bt, cu, ctx_d)
+            if plan.kind == pa.STEP_PREFILL:
+                pa.prefill(geom, out, qd, kp, vp, bt, cu, ctx_d, max_q_len=plan.max_new_len,
+                           max_ctx_len=plan.max_ctx_len, scale=SCALE, causal=True)
+            else:
+                pa.decode(geom, out, qd, kp, vp, bt, ctx_d, max_ctx_len=plan.max_ctx_len,
+                          scale=SCALE)
         torch.cuda.synchronize()
         gpu_rows.append(f32_host(out))
         ref_rows.append(np.concatenate(refs))
