@@ -80,16 +80,14 @@ struct DecodeTile {
   static constexpr int NV = BS / 8;       // 16-byte V loads per page (= dims per lane)
   uint4 k[8];
   uint4 v[PPT][NV];
-  int new_page;  // APPEND: page of the sequence's newest token if this tile holds it, else -1
 };
 
 // APPEND: one new token per sequence (the one at ctx_lens[s] - 1, rows k_new / v_new
-// [n_seqs][Hkv][64]) joins the cache in the same launch.  The wave that streams the
-// segment's last tile takes the token's K/V from those rows (they come in through lanes
-// 32..47 of the q load, so no load is added) in place of the pool slot, and writes them
-// into the slot with two buffer stores that every tile issues and whose range is empty
-// unless the tile holds the new token (equal store counts on every path, as for the result
-// stores).  No other wave reads that slot: a (page, KV head) slice belongs to one tile.
+// [n_seqs][Hkv][64]) is attended to in this launch: the wave that streams the segment's
+// last tile takes the token's K/V from those rows (they come in through lanes 32..47 of the
+// q load, so no load is added) in place of the pool slot.  The rows are written into the
+// pools by decode_merge_kernel, which runs after this kernel in the same call, so no store
+// joins the streaming loop and nothing in this kernel reads a slot being written.
 template <int BS, bool APPEND>
 __global__ __launch_bounds__(256) void decode_stream_kernel(
     uint16_t* __restrict__ out, float* __restrict__ ws_o, float2* __restrict__ ws_ml,
@@ -97,8 +95,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     const uint16_t* __restrict__ v_pool, const int32_t* __restrict__ block_tables,
     int max_blocks, const int32_t* __restrict__ ctx_lens, int n_seqs, int ctx_cap,
     int num_pages, int num_kv_heads, int n_workers, float qk_scale,
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* k_dst,
-    uint16_t* v_dst) {
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new) {
   using Tile = DecodeTile<BS>;
   constexpr int PPT = Tile::PPT;
   constexpr int NV = Tile::NV;
@@ -256,13 +253,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       if ((unsigned)pg[j] >= (unsigned)num_pages) {
         bad = true;
         pg[j] = 0;
-      }
-    }
-    if constexpr (APPEND) {
-      t.new_page = -1;
-      if (live && c.ctx > 0 && c.i == c.nt - 1) {
-        const int pgn = readlane_i(pid, ((c.ctx - 1) % kTile) / BS);
-        if ((unsigned)pgn < (unsigned)num_pages) t.new_page = pgn;
       }
     }
     int kpage = pg[0];
@@ -556,30 +546,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     bad_nxt = load_kv(nxt, c1, pid_n1, t + 1 < L);
     seg_bad |= bad_cur;
     compute(cur, cc, t & 1);
-    if constexpr (APPEND) {
-      // the new token's K row (lanes 0..7, one 16-byte piece each) and V column (lane d,
-      // dimension d) into its pool slot; an empty range unless this tile holds the token
-      const bool has = cur.new_page >= 0;
-      const int pin = has ? (cc.ctx - 1) % BS : 0;
-      const int nrec = has ? (int)(head_stride * 2) : 0;
-      const size_t base = has ? (size_t)cur.new_page * page_stride + (size_t)cc.g * head_stride : 0;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          k_dst + base, 0, nrec, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          v_dst + base, 0, nrec, kRsrcWord3);
-      // the row is read from LDS only on the tile that writes it (the stores themselves are
-      // issued on every tile)
-      u32x4_t kp = {0u, 0u, 0u, 0u};
-      uint16_t vd = 0;
-      if (__builtin_expect(has, 0)) {
-        const uint4 k4 = kvn_sh[w][t & 1][lane & 7];
-        kp = u32x4_t{k4.x, k4.y, k4.z, k4.w};
-        vd = reinterpret_cast<const uint16_t*>(&kvn_sh[w][t & 1][8])[lane];
-      }
-      __builtin_amdgcn_raw_buffer_store_b128(kp, rk, lane < 8 ? (lane * BS + pin) * 16 : nrec, 0,
-                                             0);
-      __builtin_amdgcn_raw_buffer_store_b16(vd, rv, (lane * BS + pin) * 2, 0, 0);
-    }
     const bool ends = t == L - 1 || cc.i == cc.nt - 1;
     __amdgpu_buffer_rsrc_t r_data = rsrc_none(), r_ml = rsrc_none();
     if (ends) finish(cc, seg_whole, seg_whole && cc.i == cc.nt - 1, seg_bad, r_data, r_ml);
@@ -613,12 +579,39 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 // M = max_j m_j, L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L, the sums
 // taken in ascending wave order.  Lane = head dimension; the (m, l) pairs and the
 // outputs are loaded lane-parallel.
+// With k_new set (pa_decode_append), each wave first writes the new K/V rows of the
+// (sequence, KV head) pairs seg = wid, wid + n_workers, ... into their pool slots (position
+// ctx_lens[s] - 1; nothing for an empty context or an out-of-range page id): lanes 0..7
+// store the K row's 16-byte pieces, lane d the V element of dimension d.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
-    const int2* __restrict__ ws_desc, int n_workers, int num_kv_heads) {
+    const int2* __restrict__ ws_desc, int n_workers, int num_kv_heads,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+    const int32_t* __restrict__ block_tables, int max_blocks, const int32_t* __restrict__ ctx_lens,
+    int n_seqs, int ctx_cap, int num_pages, int block_size) {
   const int wid = blockIdx.x * kDecodeWaves + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (wid >= n_workers) return;
+  if (k_new != nullptr) {
+    const size_t head_stride = (size_t)kHeadDim * block_size;
+    for (int seg = wid; seg < n_seqs * num_kv_heads; seg += n_workers) {
+      const int s = seg / num_kv_heads;
+      const int g = seg - s * num_kv_heads;
+      const int ctx = min(max(ctx_lens[s], 0), ctx_cap);
+      if (ctx == 0) continue;
+      const int page = block_tables[(size_t)s * max_blocks + (ctx - 1) / block_size];
+      if ((unsigned)page >= (unsigned)num_pages) continue;
+      const int slot = (ctx - 1) % block_size;
+      const size_t base = ((size_t)page * num_kv_heads + g) * head_stride;
+      const uint16_t* kr = k_new + (size_t)seg * kHeadDim;
+      const uint16_t* vr = v_new + (size_t)seg * kHeadDim;
+      if (lane < 8)
+        *reinterpret_cast<uint4*>(k_pool + base + ((size_t)lane * block_size + slot) * 8) =
+            *reinterpret_cast<const uint4*>(kr + 8 * lane);
+      v_pool[base + (size_t)lane * block_size + slot] = vr[lane];
+    }
+  }
+  if (wid >= n_workers || ws_desc == nullptr) return;
   const int2 desc = ws_desc[wid];
   const int seg = desc.x;
   if (seg < 0) return;
@@ -735,12 +728,10 @@ hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* ou
   auto* vp = static_cast<const uint16_t*>(v_pool);
   auto* kn = static_cast<const uint16_t*>(k_new);
   auto* vn = static_cast<const uint16_t*>(v_new);
-  auto* kd = const_cast<uint16_t*>(kp);  // written only by the appending variant
-  auto* vd = const_cast<uint16_t*>(vp);
 #define PA_DECODE_LAUNCH(B, A)                                                                  \
   hipLaunchKernelGGL((decode_stream_kernel<B, A>), grid, block, 0, stream, o, ws_o, ws_ml,      \
                      ws_desc, qq, kp, vp, block_tables, max_blocks, ctx_lens, n_seqs, ctx_cap,  \
-                     geo.num_pages, geo.num_kv_heads, workers, qk_scale, kn, vn, kd, vd)
+                     geo.num_pages, geo.num_kv_heads, workers, qk_scale, kn, vn)
   const bool append = k_new != nullptr;
   if (geo.block_size == 16) {
     if (append) PA_DECODE_LAUNCH(16, true); else PA_DECODE_LAUNCH(16, false);
@@ -749,9 +740,12 @@ hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* ou
   }
 #undef PA_DECODE_LAUNCH
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !plan.merge) return e;
+  if (e != hipSuccess || (!plan.merge && !append)) return e;
+  // the merge of cut segments, and (appending) the new rows' pool writes
   hipLaunchKernelGGL(decode_merge_kernel, grid, block, 0, stream, o, ws_o, ws_ml, ws_desc, workers,
-                     geo.num_kv_heads);
+                     geo.num_kv_heads, kn, vn, const_cast<uint16_t*>(kp),
+                     const_cast<uint16_t*>(vp), block_tables, max_blocks, ctx_lens, n_seqs,
+                     ctx_cap, geo.num_pages, geo.block_size);
   return hipGetLastError();
 }
 
