@@ -146,6 +146,27 @@ def test_decode_validation_returns_before_launch(lib):
                    ws_bytes=need - 1) == _lib.PA_ERR_WORKSPACE
 
 
+def _decode_append(lib, g=None, out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, bt=FAKE,
+                   max_blocks=4, ctx=FAKE, n=2, max_ctx=64, scale=0.125, part=0, ws=None,
+                   ws_bytes=0):
+    return lib.pa_decode_append(g or geom(), out, q, kn, vn, kp, vp, bt, max_blocks, ctx, n,
+                                max_ctx, scale, part, ws, ws_bytes, None)
+
+
+def test_decode_append_validation_returns_before_launch(lib):
+    for missing in ("out", "q", "kn", "vn", "kp", "vp", "bt", "ctx"):
+        assert _decode_append(lib, **{missing: None}) == _lib.PA_ERR_INVALID_ARG, missing
+    assert _decode_append(lib, g=geom(d=128)) == _lib.PA_ERR_UNSUPPORTED
+    assert _decode_append(lib, max_ctx=65) == _lib.PA_ERR_INVALID_ARG
+    assert _decode_append(lib, part=100) == _lib.PA_ERR_INVALID_ARG
+    assert _decode_append(lib, scale=float("inf")) == _lib.PA_ERR_INVALID_ARG
+    assert _decode_append(lib, n=-1) == _lib.PA_ERR_INVALID_ARG
+    assert _decode_append(lib, n=0, out=None, kn=None) == 0  # nothing to do
+    g = geom(num_pages=4096)  # the same workspace rule as pa_decode
+    assert _decode_append(lib, g=g, max_blocks=1024, max_ctx=16384,
+                          part=256) == _lib.PA_ERR_WORKSPACE
+
+
 def _plan_ws(n_seqs, max_ctx, hkv, part, cus=256):
     """Workspace bytes of the documented decode plan (no device here: 256 compute units)."""
     tiles = max(1, -(-max_ctx // 64))
