@@ -551,9 +551,10 @@ def main() -> int:
                 "bound": "hbm",
                 "kernel": "pa_decode_append (decode_stream_kernel<bs, append> + decode_merge_kernel)",
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": hbm_traffic(args.workload),
                 "bytes_per_launch": res["decode_bytes_per_launch"],
                 "avg_launch_ms": round(fz["kernel_ms"], 5)}
+            dec_line["traffic"] = None  # the counters are taken on the fused launch
             line["roofline_decode_only"] = dec_line
         else:
             line["roofline"] = dec_line
