@@ -188,6 +188,31 @@ class Layer:
         self.q_pre = up16(case.q_prefill) if len(case.prefill_seqs) else None
 
 
+class HeadStart:
+    """A GPU spin queued ahead of a timed eager step: while it runs, the host enqueues the
+    step's launches and events, so the kernels then run back to back and per-launch events
+    measure kernel time, not the host's launch rate.  The spin lasts twice the eager step's
+    wall time (at least 1 ms), calibrated once against events."""
+
+    def __init__(self, torch, stream, step_s: float):
+        self.torch, self.stream = torch, stream
+        self.ms = max(1.0, 2e3 * step_s)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        probe = 1 << 20
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(probe)  # first call loads the kernel
+            a.record(stream)
+            torch.cuda._sleep(probe)
+            b.record(stream)
+        b.synchronize()
+        per_ms = probe / max(a.elapsed_time(b), 1e-3)
+        self.cycles = int(per_ms * self.ms)
+
+    def __call__(self):
+        with self.torch.cuda.stream(self.stream):
+            self.torch.cuda._sleep(self.cycles)
+
+
 def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     import torch
 
@@ -229,54 +254,66 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     stream = torch.cuda.current_stream()
     scale = base.scale
 
-    ev_dec = [] if n_dec else None
-    ev_pre = [] if n_pre else None
-    ev_app = []
+    def launch_append(L, st):
+        pa.kv_append(geom, L.k_new, L.v_new, L.kp, L.vp, bt, cu_new, ctx, stream=st)
 
-    def step(record: bool, stream):
+    def launch_prefill(L, st):
+        pa.prefill(geom, out_pre, L.q_pre, L.kp, L.vp, pre_bt, cu_q, pre_ctx, max_q,
+                   max_ctx_pre, scale, causal=True, workspace=pre_ws, stream=st)
+
+    def launch_decode(L, st):
+        pa.decode(geom, out_dec, L.q_dec, L.kp, L.vp, dec_bt, dec_ctx, max_ctx_dec,
+                  scale, partition_tokens=part, workspace=ws, stream=st)
+
+    def step(stream):
         for L in layers:
-            if record:
-                a0 = torch.cuda.Event(enable_timing=True)
-                a0.record(stream)
-            pa.kv_append(geom, L.k_new, L.v_new, L.kp, L.vp, bt, cu_new, ctx, stream=stream)
+            launch_append(L, stream)
             if n_pre:
-                if record:
-                    p0 = torch.cuda.Event(enable_timing=True)
-                    p0.record(stream)
-                pa.prefill(geom, out_pre, L.q_pre, L.kp, L.vp, pre_bt, cu_q, pre_ctx, max_q,
-                           max_ctx_pre, scale, causal=True, workspace=pre_ws, stream=stream)
+                launch_prefill(L, stream)
             if n_dec:
-                if record:
-                    d0 = torch.cuda.Event(enable_timing=True)
-                    d0.record(stream)
-                pa.decode(geom, out_dec, L.q_dec, L.kp, L.vp, dec_bt, dec_ctx, max_ctx_dec,
-                          scale, partition_tokens=part, workspace=ws, stream=stream)
-            if record:
-                e = torch.cuda.Event(enable_timing=True)
-                e.record(stream)
-                ev_app.append((a0, p0 if n_pre else (d0 if n_dec else e)))
-                if n_pre:
-                    ev_pre.append((p0, d0 if n_dec else e))
-                if n_dec:
-                    ev_dec.append((d0, e))
+                launch_decode(L, stream)
 
     for _ in range(warmup):
-        step(False, stream)
+        step(stream)
     torch.cuda.synchronize()
-    # per-kernel times: eager steps with HIP events around every launch
-    log(f"timing {steps} eager steps (per-kernel events)")
+    t0 = time.perf_counter()
+    step(stream)
+    host_s = time.perf_counter() - t0  # host enqueue time of a step (an upper bound)
+    torch.cuda.synchronize()
+    log(f"timing {steps} eager steps")
     t0 = time.perf_counter()
     for _ in range(steps):
-        step(True, stream)
+        step(stream)
     torch.cuda.synchronize()
     wall_eager = time.perf_counter() - t0
+    # Per-kernel times: HIP events around a batch of one kernel's launches, one per layer
+    # (each launch repeats the step's own work: the append rewrites the same rows, prefill
+    # and decode only read the pools), queued behind a GPU spin that outlasts the host's
+    # enqueueing, so the launches run back to back and the events time the GPU alone.
+    # Events around single launches are not used: on this runtime they can read several
+    # times the kernel's duration when the host falls behind.
+    hold = HeadStart(torch, stream, host_s)
+    kinds = [("append", launch_append)] + ([("prefill", launch_prefill)] if n_pre else []) + \
+        ([("decode", launch_decode)] if n_dec else [])
+    ev = {k: [] for k, _ in kinds}
+    log(f"timing {steps} batches of each kernel ({hold.ms:.1f} ms head start)")
+    for _ in range(steps):
+        hold()
+        for k, fn in kinds:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for L in layers:
+                fn(L, stream)
+            b.record(stream)
+            ev[k].append((a, b))
+    torch.cuda.synchronize()
     # whole-step time: the same step captured once in a HIP graph and replayed, which
     # removes the host launch gaps between the 16 x 3 launches
     graph = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(stream)
     with torch.cuda.graph(graph, stream=cap):
-        step(False, cap)
+        step(cap)
     torch.cuda.synchronize()
     for _ in range(warmup):
         graph.replay()
@@ -288,8 +325,8 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    def avg_ms(pairs):
-        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) if pairs else 0.0
+    def avg_ms(pairs):  # per launch: each pair brackets one launch per layer
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) / n_layers if pairs else 0.0
 
     # A pure decode step (one new token per sequence, no prefill) also runs as one
     # pa_decode_append launch per layer: timed per launch (events) and as a graph, and
@@ -298,24 +335,24 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     if n_dec and not n_pre and int(base.cu_new_lens[-1]) == n_dec:
         hkv = base.num_kv_heads
 
-        def fused_step(st, ev=None):
+        def fused_step(st):
             for L in layers:
-                if ev is not None:
-                    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a0.record(st)
                 pa.decode_append(geom, out_dec, L.q_dec, L.k_new.view(n_dec, hkv, 64),
                                  L.v_new.view(n_dec, hkv, 64), L.kp, L.vp, dec_bt, dec_ctx,
                                  max_ctx_dec, scale, partition_tokens=part, workspace=ws,
                                  stream=st)
-                if ev is not None:
-                    a1.record(st)
-                    ev.append((a0, a1))
 
         ev_fused = []
         for _ in range(warmup):
             fused_step(stream)
-        for _ in range(steps):
-            fused_step(stream, ev_fused)
+        torch.cuda.synchronize()
+        for _ in range(steps):  # a batch of one launch per layer, as above
+            hold()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fused_step(stream)
+            b.record(stream)
+            ev_fused.append((a, b))
         torch.cuda.synchronize()
         graph_f = torch.cuda.CUDAGraph()
         cap_f = torch.cuda.Stream()
@@ -336,11 +373,11 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
 
     ms_step = wall * 1e3 / steps
     res = {"ms_per_step": ms_step, "ms_per_step_eager": wall_eager * 1e3 / steps,
-           "n_layers": n_layers, "partition_tokens": part, "append_ms": avg_ms(ev_app),
+           "n_layers": n_layers, "partition_tokens": part, "append_ms": avg_ms(ev["append"]),
            "fused": fused}
     kv_bytes_layer = base.kv_tokens() * KV_BYTES_PER_TOKEN
     if n_dec:
-        dec_ms = avg_ms(ev_dec)
+        dec_ms = avg_ms(ev["decode"])
         res.update(decode_ms=dec_ms, decode_bytes_per_launch=kv_bytes_layer,
                    decode_gbps=kv_bytes_layer / (dec_ms * 1e-3) / 1e9,
                    value=kv_bytes_layer * n_layers / (ms_step * 1e-3) / 1e9, unit="GB/s")
@@ -350,7 +387,7 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
                          separate_value=res["value"], separate_ms_per_step=ms_step)
             res.update(value=fused["value"], ms_per_step=fused["ms_per_step"])
     if n_pre:
-        pre_ms = avg_ms(ev_pre)
+        pre_ms = avg_ms(ev["prefill"])
         flops = base.prefill_pairs() * FLOP_PER_PAIR
         res.update(prefill_ms=pre_ms, prefill_flop_per_launch=flops,
                    prefill_tflops=flops / (pre_ms * 1e-3) / 1e12)
@@ -367,21 +404,32 @@ def n_copies(footprint: int) -> int:
 
 
 def timed_rotating(fns, steps: int, stream) -> float:
-    """Average HIP-event time of one launch over ``steps`` back-to-back launches that
-    cycle through ``fns`` (one closure per buffer set)."""
+    """Average HIP-event time of one launch over ``steps`` launches that cycle through
+    ``fns`` (one closure per buffer set): events around batches of 16 back-to-back launches,
+    each batch queued behind a head start (``HeadStart``) so that none of them waits for the
+    host."""
     import torch
 
+    t0 = time.perf_counter()
     for fn in fns:
         fn()
-    ev = []
-    for i in range(steps):
+    host_s = (time.perf_counter() - t0) / len(fns)  # host enqueue time per launch (upper bound)
+    torch.cuda.synchronize()
+    chunk = 16
+    hold = HeadStart(torch, stream, host_s * chunk)
+    ev, i = [], 0
+    while i < steps:
+        n = min(chunk, steps - i)
+        hold()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        fns[i % len(fns)]()
+        for k in range(n):
+            fns[(i + k) % len(fns)]()
         b.record(stream)
-        ev.append((a, b))
+        ev.append((a, b, n))
+        i += n
     torch.cuda.synchronize()
-    return float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    return float(sum(x.elapsed_time(y) for x, y, _ in ev) / sum(n for _, _, n in ev))
 
 
 def run_rope(cfg: int, steps: int, warmup: int) -> dict:
@@ -708,7 +756,8 @@ def run_serve() -> dict:
     """The slot scheduler (pa_sched_step) driving pa_kv_append + pa_prefill / pa_decode on
     each of SERVE_LAYERS layers over SERVE_REQS requests until all have finished: every
     plan is uploaded once and run as is.
-    Kernels are timed with HIP events; the scheduler's own host time is measured apart."""
+    The stream runs twice: once for the wall time and the scheduler's own host time, once
+    with each step's kernels timed by HIP events around their batch."""
     import torch
 
     import paged_kv_attention_31_amd as pa
@@ -727,54 +776,71 @@ def run_serve() -> dict:
     v_src = torch.empty_like(k_src).normal_()
     q_src = torch.empty((rows_max, 32, 64), dtype=torch.bfloat16, device=dev).normal_()
     out = torch.empty_like(q_src)
-    pool = pa.PagePool(n_pages)
-    sched = pa.Scheduler(pool, SERVE_SLOTS, SERVE_BS, max_blocks, SERVE_CHUNK)
-    for rid, (p, m) in enumerate(zip(prompts, news)):
-        sched.submit(rid, p, m)
     stream = torch.cuda.current_stream()
-    ev = {pa.STEP_PREFILL: [], pa.STEP_DECODE: []}
-    kv_bytes = pairs = 0
-    n_steps = {pa.STEP_PREFILL: 0, pa.STEP_DECODE: 0}
-    sched_s = 0.0
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    while True:
-        a = time.perf_counter()
-        plan = sched.step()
-        sched_s += time.perf_counter() - a
-        if plan.kind == pa.STEP_IDLE:
-            if sched.pending() == 0:
-                break
-            continue
-        n = len(plan.req_ids)
-        t = int(plan.cu_new_lens[-1])
-        bt = torch.from_numpy(plan.block_tables).to(dev)
-        ctx = torch.from_numpy(plan.ctx_lens).to(dev)
-        cu = torch.from_numpy(plan.cu_new_lens).to(dev)
-        for kp, vp in pools:  # one block table serves every layer
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def serve_pass(hold=None):
+        """Run the request stream through a fresh pool and scheduler.  With ``hold`` the
+        kernels of each step (one launch per layer) are timed as one batch between HIP
+        events, queued behind that head start; a prefill step's appends run before it."""
+        pool = pa.PagePool(n_pages)
+        sched = pa.Scheduler(pool, SERVE_SLOTS, SERVE_BS, max_blocks, SERVE_CHUNK)
+        for rid, (p, m) in enumerate(zip(prompts, news)):
+            sched.submit(rid, p, m)
+        ev = {pa.STEP_PREFILL: [], pa.STEP_DECODE: []}
+        kv_bytes = pairs = 0
+        n_steps = {pa.STEP_PREFILL: 0, pa.STEP_DECODE: 0}
+        sched_s, host_s = 0.0, 0.0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while True:
+            a = time.perf_counter()
+            plan = sched.step()
+            sched_s += time.perf_counter() - a
+            if plan.kind == pa.STEP_IDLE:
+                if sched.pending() == 0:
+                    break
+                continue
+            n = len(plan.req_ids)
+            t = int(plan.cu_new_lens[-1])
+            bt = torch.from_numpy(plan.block_tables).to(dev)
+            ctx = torch.from_numpy(plan.ctx_lens).to(dev)
+            cu = torch.from_numpy(plan.cu_new_lens).to(dev)
+            if plan.kind == pa.STEP_PREFILL:  # one block table serves every layer
+                for kp, vp in pools:
+                    pa.kv_append(geom, k_src[:t], v_src[:t], kp, vp, bt, cu, ctx, stream=stream)
+            if hold is not None:
+                hold()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            a = time.perf_counter()
+            for kp, vp in pools:
+                if plan.kind == pa.STEP_PREFILL:
+                    pa.prefill(geom, out[:t], q_src[:t], kp, vp, bt, cu, ctx, plan.max_new_len,
+                               plan.max_ctx_len, 0.125, causal=True, stream=stream)
+                else:  # one new token per row: append and attend in one launch
+                    pa.decode_append(geom, out[:n], q_src[:n], k_src[:n], v_src[:n], kp, vp, bt,
+                                     ctx, plan.max_ctx_len, 0.125, stream=stream)
+            host_s = max(host_s, time.perf_counter() - a)
+            if hold is not None:
+                e1.record(stream)
+                ev[plan.kind].append((e0, e1))
             if plan.kind == pa.STEP_PREFILL:
-                pa.kv_append(geom, k_src[:t], v_src[:t], kp, vp, bt, cu, ctx, stream=stream)
-                e0.record(stream)
-                pa.prefill(geom, out[:t], q_src[:t], kp, vp, bt, cu, ctx, plan.max_new_len,
-                           plan.max_ctx_len, 0.125, causal=True, stream=stream)
-            else:  # one new token per row: append and attend in one launch
-                e0.record(stream)
-                pa.decode_append(geom, out[:n], q_src[:n], k_src[:n], v_src[:n], kp, vp, bt,
-                                 ctx, plan.max_ctx_len, 0.125, stream=stream)
-            e1.record(stream)
-            ev[plan.kind].append((e0, e1))
-        if plan.kind == pa.STEP_PREFILL:
-            lens = np.diff(plan.cu_new_lens).astype(np.int64)
-            c = plan.ctx_lens.astype(np.int64)
-            pairs += SERVE_LAYERS * int(np.sum(lens * (c - lens) + lens * (lens + 1) // 2))
-        else:
-            kv_bytes += (SERVE_LAYERS * int(plan.ctx_lens.astype(np.int64).sum())
-                         * KV_BYTES_PER_TOKEN)
-        n_steps[plan.kind] += 1
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    sched.close()
+                lens = np.diff(plan.cu_new_lens).astype(np.int64)
+                c = plan.ctx_lens.astype(np.int64)
+                pairs += SERVE_LAYERS * int(np.sum(lens * (c - lens) + lens * (lens + 1) // 2))
+            else:
+                kv_bytes += (SERVE_LAYERS * int(plan.ctx_lens.astype(np.int64).sum())
+                             * KV_BYTES_PER_TOKEN)
+            n_steps[plan.kind] += 1
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        sched.close()
+        return ev, kv_bytes, pairs, n_steps, sched_s, wall, host_s
+
+    # pass 1: wall time and scheduler time, no events; pass 2: the same stream again, each
+    # step's kernels timed as one batch behind a head start
+    _, kv_bytes, pairs, n_steps, sched_s, wall, host_s = serve_pass()
+    ev = serve_pass(HeadStart(torch, stream, host_s))[0]
     dec_ms = sum(x.elapsed_time(y) for x, y in ev[pa.STEP_DECODE])
     pre_ms = sum(x.elapsed_time(y) for x, y in ev[pa.STEP_PREFILL])
     steps = n_steps[pa.STEP_PREFILL] + n_steps[pa.STEP_DECODE]
