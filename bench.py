@@ -113,6 +113,38 @@ def hbm_traffic(key: str):
     return round(float(entry["bytes_per_launch"]))
 
 
+def unique_kv_bytes(case: W.Case) -> int:
+    """Decode KV bytes with pages shared by several sequences counted once (the logical
+    figure, ``kv_tokens() * 2048``, counts them once per sequence that reads them)."""
+    r = case.decode_seqs
+    n_shared = len([s for s in case.shared_seqs if r.start <= s < r.stop])
+    dup = max(n_shared - 1, 0) * case.shared_prefix_tokens
+    return (case.kv_tokens() - dup) * KV_BYTES_PER_TOKEN
+
+
+def prefill_min_bytes(case: W.Case) -> int:
+    """HBM bytes a prefill launch cannot avoid: its q rows read and output rows written once
+    (32 heads x 64 dims x bf16 each) and every prefill sequence's K/V read once."""
+    p = case.prefill_seqs
+    rows = int(case.q_lens_prefill.sum())
+    ctx = int(case.ctx_lens[p.start:p.stop].astype(np.int64).sum())
+    return 2 * rows * 32 * 64 * 2 + ctx * KV_BYTES_PER_TOKEN
+
+
+def host_cpu() -> dict:
+    """The host's CPU model and numpy's version, reported with the oracle baseline."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "numpy": np.__version__}
+
+
 # ---------------------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, single thread, bounded sample
 # ---------------------------------------------------------------------------------------
@@ -587,6 +619,7 @@ def main() -> int:
                     "frac": round(ach / HBM_PEAK_GBPS, 4),
                     "traffic": hbm_traffic(args.workload),
                     "bytes_per_launch": res["decode_bytes_per_launch"],
+                    "unique_bytes_per_launch": unique_kv_bytes(base),
                     "avg_launch_ms": round(res["decode_ms"], 5)}
         fz = res.get("fused")
         if fz is not None:
@@ -601,6 +634,7 @@ def main() -> int:
                 "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": hbm_traffic(args.workload),
                 "bytes_per_launch": res["decode_bytes_per_launch"],
+                "unique_bytes_per_launch": unique_kv_bytes(base),
                 "avg_launch_ms": round(fz["kernel_ms"], 5)}
             dec_line["traffic"] = None  # the counters are taken on the fused launch
             line["roofline_decode_only"] = dec_line
@@ -617,8 +651,14 @@ def main() -> int:
                                             else args.workload),
                      "flop_per_launch": res["prefill_flop_per_launch"],
                      "avg_launch_ms": round(res["prefill_ms"], 5)}
+        # the least HBM traffic a prefill launch needs (q and out once, each sequence's K/V
+        # once) at the measured time, against HBM peak: the other bound this launch is near
+        min_b = prefill_min_bytes(base)
+        gbps = min_b / (res["prefill_ms"] * 1e-3) / 1e9
+        line[key].update(hbm_min_bytes=min_b, hbm_min_gbps=round(gbps, 1),
+                         hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
     line["append_ms_per_layer"] = round(res["append_ms"], 5)
-    line["cpu_baseline"] = cpu
+    line["cpu_baseline"] = dict(cpu, **host_cpu()) if cpu else cpu
     print(json.dumps(line), flush=True)
     return 0
 
@@ -688,7 +728,7 @@ def main_copy(args) -> int:
                      "traffic": hbm_traffic("copy-pages"),
                      "bytes_per_launch": res["bytes_per_launch"],
                      "avg_launch_ms": round(res["ms"], 5)},
-        "cpu_baseline": cpu,
+        "cpu_baseline": dict(cpu, **host_cpu()) if cpu else cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -922,7 +962,7 @@ def main_serve(args) -> int:
                   "generated_tokens_per_s": round(res["tokens"] / res["wall_s"], 1),
                   "prefill_tflops": round(res["prefill_tflops"], 1),
                   "prefill_kernel_ms_total": round(res["prefill_ms"], 3)},
-        "cpu_baseline": cpu,
+        "cpu_baseline": dict(cpu, **host_cpu()) if cpu else cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -949,7 +989,7 @@ def main_norm(args) -> int:
                              "avg_launch_ms": round(res["norm_ms"], 5),
                              "achieved_gbps": round(res["norm_gbps"], 1),
                              "frac": round(res["norm_gbps"] / HBM_PEAK_GBPS, 4)},
-        "cpu_baseline": cpu,
+        "cpu_baseline": dict(cpu, **host_cpu()) if cpu else cpu,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -1018,7 +1058,7 @@ def main_rope(args, cfg: int) -> int:
         "plain_append": {"kernel": "pa_kv_append", "bytes_per_launch": res["plain_bytes_per_launch"],
                          "avg_launch_ms": round(res["plain_ms"], 5),
                          "achieved_gbps": round(res["plain_gbps"], 1)},
-        "cpu_baseline": cpu,
+        "cpu_baseline": dict(cpu, **host_cpu()) if cpu else cpu,
     }
     print(json.dumps(line), flush=True)
     return 0

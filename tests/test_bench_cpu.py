@@ -84,3 +84,21 @@ def test_workload_5_mixed_step():
     others = [s for s in range(c.n_seqs) if s not in set(c.shared_seqs.tolist())]
     assert not set(first[0].tolist()) & set(
         np.concatenate([c.block_tables[s, : need[s]] for s in others]).tolist())
+
+
+def test_reported_byte_counts():
+    """The unique-KV and minimum-prefill-traffic figures printed beside the algorithmic ones:
+    workload 5's 32 sequences read one 256-token prefix, so 31 x 256 tokens x 2048 B fewer
+    unique bytes; workload 3 moves q and out once (ΣL rows x 4096 B each) and K/V once
+    (ΣL x 2048 B)."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    c5 = W.make_case(5, values=False)
+    assert c5.kv_tokens() * 2048 - bench.unique_kv_bytes(c5) == 31 * 256 * 2048
+    c3 = W.make_case(3, values=False)
+    total = int(c3.ctx_lens.sum())
+    assert bench.prefill_min_bytes(c3) == total * (2 * 4096 + 2048)
+    for cfg in (2, 4):
+        c = W.make_case(cfg, values=False)
+        assert bench.unique_kv_bytes(c) == c.kv_tokens() * 2048  # nothing shared
