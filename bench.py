@@ -562,7 +562,7 @@ def main() -> int:
                          "(HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
               "multi-GPU path; the attention shards by sequence or KV head with no exchange",
               file=sys.stderr)
         return 2

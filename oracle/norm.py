@@ -19,7 +19,7 @@ What is computed (per token row of H values):
     h is also returned, as the next sub-layer's residual);
   * out = silu(g) * u with silu(z) = z / (1 + e^-z)          (the gated MLP activation).
 
-Readings taken where the pages are silent (each one is also listed in the design doc):
+Readings taken where the pages are silent:
   * the residual sum is rounded to bf16 before it is normalised (it is stored as the next
     residual in bf16, and the normalisation reads that stored value);
   * mean(h^2), the scaling and the products run in full precision and each output is

@@ -17,7 +17,7 @@ gather the pages back into contiguous K/V, then causal grouped-query softmax att
 ([guide] §Llama 3.2 1B架构拆解: GQA, causal mask, softmax, weighted sum of V), with
 the new token's K/V appended before it attends ([guide] §推理流程：从Prefill到Decode).
 
-Readings taken where the pages are silent (each one is also listed in the design doc):
+Readings taken where the pages are silent:
   * query head h reads KV head h // (Hq / Hkv) (contiguous groups);
   * scores are scaled by ``scale`` (1/sqrt(64) = 1/8) before the max;
   * a query at absolute position p sees keys 0..p inclusive (bottom-right causal);

@@ -16,7 +16,7 @@ place: the writer first takes a fresh page, copies the shared page's K and V int
 points its own block-table entry at the copy, dropping one reference from the original.
 A page with a single reference is written in place.
 
-Readings taken where the pages are silent (each one is also listed in the design doc):
+Readings taken where the pages are silent:
   * a copy moves the whole page (every KV head, every slot) of both pools, bit for bit;
   * the decision is taken per block-table entry, in order: an entry whose page has more
     than one reference at its turn gets a copy and lowers that count by one.

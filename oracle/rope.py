@@ -17,7 +17,7 @@ turned through the angle p * f_i, where p is the token's absolute position in it
 sequence.  The rotated K joins the page cache exactly where the plain append would put
 it; V is copied unchanged; Q is rotated with the same positions and returned.
 
-Readings taken where the pages are silent (each one is also listed in the design doc):
+Readings taken where the pages are silent:
   * pair i is (x[i], x[i + d/2]) ("rotate half"), turned counter-clockwise:
     (a, b) -> (a cos t - b sin t, b cos t + a sin t);
   * f_i = theta ** (-2 i / d) with a caller-given base theta (500000 for the Llama 3

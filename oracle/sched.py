@@ -17,7 +17,7 @@ Sources (cited by title and section):
   [实战]  §内存池管理: a preallocated pool hands pages out and takes them back when a
           request ends.
 
-What a step does (this oracle's reading; each item is also listed in the design doc):
+What a step does (this oracle's reading):
   1. Retire: a request that has produced its max_new tokens, or that the caller finished,
      returns its pages to the pool and frees its slot.
   2. Admit: while a slot is free, the oldest waiting request enters it (lowest free slot
