@@ -88,9 +88,9 @@ def test_workload_5_mixed_step():
 
 def test_reported_byte_counts():
     """The unique-KV and minimum-prefill-traffic figures printed beside the algorithmic ones:
-    workload 5's 32 sequences read one 256-token prefix, so 31 x 256 tokens x 2048 B fewer
-    unique bytes; workload 3 moves q and out once (ΣL rows x 4096 B each) and K/V once
-    (ΣL x 2048 B)."""
+    in the 16-layer mixed step 32 decode sequences read one 256-token prefix, so 31 x 256
+    tokens x 2048 B fewer unique bytes; the 8-prompt prefill moves q and out once (ΣL rows x
+    4096 B each) and K/V once (ΣL x 2048 B)."""
     sys.path.insert(0, ROOT)
     import bench
 
