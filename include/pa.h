@@ -281,7 +281,10 @@ int pa_decode(pa_geom_t g, void* out, const void* q, const void* k_pool, const v
  * included.  Outputs and pools equal, bit for bit, those of pa_kv_append
  * (cu_new_lens = 0, 1, ..., n_seqs) followed by pa_decode with the same arguments.
  * Every other argument, the workspace and the errors are as for pa_decode; k_pool /
- * v_pool are written.  ctx_lens[s] must not exceed max_ctx_len.
+ * v_pool are written.  ctx_lens[s] must not exceed max_ctx_len (nor max_blocks_per_seq *
+ * block_size): a sequence past that bound is not clamped as pa_decode clamps it, since
+ * its new token would land on a cached one; nothing is written for it and its output
+ * row is NaN.
  * ------------------------------------------------------------------------------- */
 int pa_decode_append(pa_geom_t g, void* out, const void* q, const void* k_new,
                      const void* v_new, void* k_pool, void* v_pool,

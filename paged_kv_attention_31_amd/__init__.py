@@ -213,6 +213,22 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _scratch(need: int, device, stream):
+    """A uint8 workspace of ``need`` bytes allocated here for one call on ``stream``.
+    torch's caching allocator ties a block to the stream it was allocated on (the current
+    one); when the kernels run on another stream the block is recorded on that stream too,
+    so it is not handed out again before the kernels that write it have finished."""
+    import torch
+
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if stream is not None:
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
+            int(stream), device=device)
+        if s.cuda_stream != torch.cuda.current_stream(device).cuda_stream:
+            ws.record_stream(s)
+    return ws
+
+
 def _need(cond: bool, what: str) -> None:
     if not cond:
         raise ValueError(what)
@@ -371,7 +387,7 @@ def decode(geom: Geometry, out, q, k_pool, v_pool, block_tables, ctx_lens, max_c
     _need(block_tables.shape[0] == n, "block_tables rows != n_seqs")
     need = decode_workspace_bytes(geom, n, int(max_ctx_len), int(partition_tokens))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
@@ -404,7 +420,7 @@ def decode_append(geom: Geometry, out, q, k_new, v_new, k_pool, v_pool, block_ta
     _need(block_tables.shape[0] == n, "block_tables rows != n_seqs")
     need = decode_workspace_bytes(geom, n, int(max_ctx_len), int(partition_tokens))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
@@ -443,7 +459,7 @@ def prefill(geom: Geometry, out, q, k_pool, v_pool, block_tables, cu_q_lens, ctx
     _need(block_tables.shape[0] == n, "block_tables rows != n_seqs")
     need = prefill_workspace_bytes(geom, n, int(max_q_len), int(max_ctx_len), int(kv_splits))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream)
     ws_bytes = 0
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)

@@ -70,6 +70,7 @@ struct Cursor {
   int ctx;        // context length of s (clamped)
   int nt;         // tiles per KV head of s
   int64_t first;  // stream index of the first tile of sequence s
+  bool over;      // APPEND: ctx_lens[s] exceeds the cap (output NaN, nothing appended)
 };
 
 // K and V registers of one tile: lane t holds the K row of token t; for V, the lane holds
@@ -109,11 +110,16 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   const int hq = hkv * kGroup;
   // values read from LDS at a wave-uniform address, kept in SGPRs
   auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  // A context length as held below: clamped to [0, ctx_cap], except that with APPEND a
+  // length past the cap reads ctx_cap + 1 (the sequence is then marked, not clamped:
+  // its new token has no slot below the cap).
+  auto ctx_code = [&](int raw) { return min(max(raw, 0), APPEND ? ctx_cap + 1 : ctx_cap); };
 
   __shared__ int scan_sh[257];
   __shared__ int wsum_sh[kDecodeWaves];
   __shared__ uint4 q_sh[kDecodeWaves][2][kGroup][8];  // [wave][slot][head][piece]
-  __shared__ __attribute__((aligned(16))) uint16_t p_sh[kDecodeWaves][kGroup][64];
+  // probabilities of the tile as two bf16 terms, p = hi + lo: [wave][term][head][token]
+  __shared__ __attribute__((aligned(16))) uint16_t p_sh[kDecodeWaves][2][kGroup][64];
   __shared__ __attribute__((aligned(16))) float fin_sh[kDecodeWaves][kGroup * kHeadDim];
   __shared__ float2 fin_ml[kDecodeWaves][kGroup];
   __shared__ uint4 kvn_sh[kDecodeWaves][2][16];  // APPEND: new K (8 pieces), then V (8 pieces)
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   int mine = 0;
   for (int j = 0; j < chunk; ++j) {
     const int s = tid * chunk + j;
-    if (s < n_seqs) mine += tiles_of(min(max(ctx_lens[s], 0), ctx_cap));
+    if (s < n_seqs) mine += tiles_of(min(ctx_code(ctx_lens[s]), ctx_cap));
   }
   int incl = mine;
 #pragma unroll
@@ -160,12 +166,12 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     const int mid = (lo + hi + 1) >> 1;
     if ((int64_t)uni(scan_sh[mid]) * hkv <= a) lo = mid; else hi = mid - 1;
   }
-  Cursor cc{-1, 0, 0, 0, 1, 0};
+  Cursor cc{-1, 0, 0, 0, 1, 0, false};
   int64_t cum = uni(scan_sh[lo]);
   for (int s0 = lo * chunk; s0 < n_seqs; s0 += 64) {
     const int sj = s0 + lane;
-    const int cj = sj < n_seqs ? min(max(ctx_lens[sj], 0), ctx_cap) : 0;
-    const int nj = sj < n_seqs ? tiles_of(cj) : 0;
+    const int cj = sj < n_seqs ? ctx_code(ctx_lens[sj]) : 0;
+    const int nj = sj < n_seqs ? tiles_of(min(cj, ctx_cap)) : 0;
     int pre = nj;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -176,7 +182,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     if (hit) {
       const int j = __ffsll((unsigned long long)hit) - 1;
       cc.s = s0 + j;
-      cc.ctx = readlane_i(cj, j);
+      const int code = readlane_i(cj, j);
+      cc.ctx = min(code, ctx_cap);
+      cc.over = code > ctx_cap;
       cc.nt = readlane_i(nj, j);
       cum += readlane_i(pre - nj, j);
       break;
@@ -194,8 +202,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   // tiles long (the host sizes the worker count for that) and every sequence holds at
   // least Hkv tiles, so a range touches at most 58 sequences.
   const int cache_base = cc.s;
-  const int cache_ctx =
-      cache_base + lane < n_seqs ? min(max(ctx_lens[cache_base + lane], 0), ctx_cap) : 0;
+  const int cache_ctx = cache_base + lane < n_seqs ? ctx_code(ctx_lens[cache_base + lane]) : 0;
   auto advance = [&](Cursor& c) {
     if (++c.i == c.nt) {
       c.i = 0;
@@ -203,7 +210,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
         c.g = 0;
         c.first += (int64_t)hkv * c.nt;
         ++c.s;
-        c.ctx = readlane_i(cache_ctx, min(c.s - cache_base, 63));
+        const int code = readlane_i(cache_ctx, min(c.s - cache_base, 63));
+        c.ctx = min(code, ctx_cap);
+        c.over = code > ctx_cap;
         c.nt = tiles_of(c.ctx);
       }
     }
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   // Returns true if a page id is out of range (page 0 is read instead).
   auto load_kv = [&](Tile& t, const Cursor& c, int pid, bool live) -> bool {
     int pg[PPT];
-    bool bad = false;
+    bool bad = APPEND && c.over;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       pg[j] = readlane_i(pid, j);
@@ -288,7 +297,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   auto compute = [&](Tile& t, const Cursor& c, int slot) {
     const int nvalid = min(max(c.ctx - c.i * kTile, 0), kTile);
     if constexpr (APPEND) {
-      if (c.ctx > 0 && c.i == c.nt - 1) {  // uniform: the tile holds the newest token
+      if (c.ctx > 0 && c.i == c.nt - 1 && !c.over) {  // uniform: the tile holds the newest token
         const int pn = nvalid - 1;           // its index in the tile
         if (lane == pn) {
 #pragma unroll
@@ -353,8 +362,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 
     // Online-softmax update.  The tile maxima are wave-uniform, so the rescale of the
     // running sums and outputs is one uniform branch, skipped when no head's maximum
-    // grew.  p is rounded to bf16 once; the same rounded value feeds both the running
-    // sum and the P.V product, so the output is an exact convex combination of V rows.
+    // grew.  p goes to P.V as two bf16 terms, hi = bf16(p) and lo = bf16(p - hi), so
+    // the weights keep 16 significant bits (one bf16 term alone, 8 bits, can move the
+    // output of a row dominated by a few keys by 2^-8 of the spread of their V values);
+    // the running sum adds the same hi + lo, so the output is an exact convex
+    // combination of V rows.
     float mt[kGroup] = {x[0], x[1], x[2], x[3]};
     wave_max4(mt[0], mt[1], mt[2], mt[3]);
     if (mt[0] > m[0] || mt[1] > m[1] || mt[2] > m[2] || mt[3] > m[3]) {
@@ -371,40 +383,56 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 #pragma unroll
     for (int h = 0; h < kGroup; ++h) {
       const float mref = m[h] == kNegInf ? 0.f : m[h];  // a tile with no key keeps m = -inf
-      const uint16_t pb = to_bf16(fast_exp2(x[h] - mref));  // 0 for tokens past the end
-      l[h] += __uint_as_float((uint32_t)pb << 16);
-      p_sh[w][h][lane] = pb;
+      const float p = fast_exp2(x[h] - mref);           // 0 for tokens past the end
+      const uint16_t ph = to_bf16(p);
+      const float phf = __uint_as_float((uint32_t)ph << 16);
+      const uint16_t pl = to_bf16(p - phf);
+      l[h] += phf + __uint_as_float((uint32_t)pl << 16);
+      p_sh[w][0][h][lane] = ph;
+      p_sh[w][1][h][lane] = pl;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+    if (nvalid < kTile) {
+      // tokens past the end may hold stale bytes (even NaN): clear them
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int tb = j * BS + (lane % LPR) * 8;  // tile index of this lane's first token
-      uint4 pp[kGroup];
+      for (int j = 0; j < PPT; ++j) {
+        const int tb = j * BS + (lane % LPR) * 8;  // tile index of this lane's first token
 #pragma unroll
-      for (int h = 0; h < kGroup; ++h) pp[h] = *reinterpret_cast<const uint4*>(&p_sh[w][h][tb]);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        uint4 vv = t.v[j][i];
-        if (nvalid < kTile) {
-          // tokens past the end may hold stale bytes (even NaN): clear them
-          uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+        for (int i = 0; i < NV; ++i) {
+          uint32_t wv[4] = {t.v[j][i].x, t.v[j][i].y, t.v[j][i].z, t.v[j][i].w};
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             if (tb + k >= nvalid) wv[k >> 1] &= (k & 1) ? 0x0000ffffu : 0xffff0000u;
           }
-          vv = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+          t.v[j][i] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
         }
+      }
+    }
+    // P.V over the hi terms, then over the lo terms
 #pragma unroll
-        for (int h = 0; h < kGroup; ++h) {
-          float a = acc[i][h];
-          a = dot2(vv.x, pp[h].x, a);
-          a = dot2(vv.y, pp[h].y, a);
-          a = dot2(vv.z, pp[h].z, a);
-          a = dot2(vv.w, pp[h].w, a);
-          acc[i][h] = a;
+    for (int part = 0; part < 2; ++part) {
+#pragma unroll
+      for (int j = 0; j < PPT; ++j) {
+        const int tb = j * BS + (lane % LPR) * 8;
+        uint4 pp[kGroup];
+#pragma unroll
+        for (int h = 0; h < kGroup; ++h)
+          pp[h] = *reinterpret_cast<const uint4*>(&p_sh[w][part][h][tb]);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const uint4 vv = t.v[j][i];
+#pragma unroll
+          for (int h = 0; h < kGroup; ++h) {
+            float a = acc[i][h];
+            a = dot2(vv.x, pp[h].x, a);
+            a = dot2(vv.y, pp[h].y, a);
+            a = dot2(vv.z, pp[h].z, a);
+            a = dot2(vv.w, pp[h].w, a);
+            acc[i][h] = a;
+          }
         }
       }
     }
@@ -592,13 +620,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     int n_seqs, int ctx_cap, int num_pages, int block_size) {
   const int wid = blockIdx.x * kDecodeWaves + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (k_new != nullptr) {
+  if (k_new != nullptr && wid < n_workers) {  // each (sequence, KV head) row written once
     const size_t head_stride = (size_t)kHeadDim * block_size;
     for (int seg = wid; seg < n_seqs * num_kv_heads; seg += n_workers) {
       const int s = seg / num_kv_heads;
       const int g = seg - s * num_kv_heads;
-      const int ctx = min(max(ctx_lens[s], 0), ctx_cap);
-      if (ctx == 0) continue;
+      const int raw = ctx_lens[s];
+      if (raw > ctx_cap || raw <= 0) continue;  // past the cap: no slot (output is NaN)
+      const int ctx = raw;
       const int page = block_tables[(size_t)s * max_blocks + (ctx - 1) / block_size];
       if ((unsigned)page >= (unsigned)num_pages) continue;
       const int slot = (ctx - 1) % block_size;

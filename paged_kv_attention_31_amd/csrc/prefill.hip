@@ -133,6 +133,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int kend = causal ? min(ctx, pos_last + 1) : ctx;    // keys [0, kend)
   const int klim = causal ? min(ctx, qpos + 1) : ctx;        // this lane's row sees keys < klim
   const int n_all = (kend + kStage - 1) / kStage;       // stages of the whole tile
+  // A row that sees few keys gets its output from a few large weights, and one bf16
+  // term per probability (8 significant bits) can then move it by 2^-8 of the spread of
+  // those keys' V values.  Tiles holding a row that sees fewer than 64 keys therefore
+  // feed P.V two bf16 terms per probability (hi = bf16(p), lo = bf16(p - hi): 16 bits).
+  const bool precise = (causal ? min(ctx, pos_first + 1) : ctx) < kStage;
   const int st0 = piece * n_all / n_split;              // this piece: stages st0 .. +n_stages
   const int n_stages = (piece + 1) * n_all / n_split - st0;
   const int last_blk = kend > 0 ? (kend - 1) / BS : 0;
@@ -256,9 +261,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
                                                      qb[st], sacc, 0, 0, 0);
     return sacc;
   };
-  // mask, online-softmax update; returns p (bf16 pairs) in the S^T accumulator order
-  auto softmax = [&](const f32x16_t& sacc, int kb, uint32_t (&pk)[8])
-      __attribute__((always_inline)) {
+  // mask, online-softmax update; returns p (bf16 pairs) in the S^T accumulator order, and
+  // with `precise` also the pairs of the remainders p - hi in pl
+  auto softmax = [&](const f32x16_t& sacc, int kb, uint32_t (&pk)[8], uint32_t (&pl)[8],
+                     auto precise_tag) __attribute__((always_inline)) {
+    constexpr bool PRECISE = decltype(precise_tag)::value;
     float sv[16];
     if ((kb + 32 > ctx) || (causal && kb + 31 > pos_first)) {  // the half crosses a limit
       // element r is key kb + 8 (r / 4) + 4 half + r % 4, visible while below klim
@@ -295,12 +302,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     }
     // p = 2^(s * qk_scale - m), rounded to bf16 once: the P.V operand; the running sum
     // adds those same rounded values (a dot with (1, 1)), so the normaliser matches.
+    if constexpr (PRECISE) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      pk[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(sv[2 * i], qk_scale, negm)),
-                          fast_exp2(__builtin_fmaf(sv[2 * i + 1], qk_scale, negm)));
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = fast_exp2(__builtin_fmaf(sv[2 * i], qk_scale, negm));
+        const float p1 = fast_exp2(__builtin_fmaf(sv[2 * i + 1], qk_scale, negm));
+        pk[i] = pack_bf16x2(p0, p1);
+        pl[i] = pack_bf16x2(p0 - bf_lo(pk[i]), p1 - bf_hi(pk[i]));
+      }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lsum = dot2(pk[i], 0x3F803F80u, lsum);
+      for (int i = 0; i < 8; ++i) {
+        lsum = dot2(pk[i], 0x3F803F80u, lsum);
+        lsum = dot2(pl[i], 0x3F803F80u, lsum);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pk[i] = pack_bf16x2(fast_exp2(__builtin_fmaf(sv[2 * i], qk_scale, negm)),
+                            fast_exp2(__builtin_fmaf(sv[2 * i + 1], qk_scale, negm)));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lsum = dot2(pk[i], 0x3F803F80u, lsum);
+    }
   };
   // O^T += V^T . P^T.  Element e (0..7) of lane half h's B operand for k-step ks is the
   // score of key 16 ks + (e < 4 ? 0 : 8) + 4 h + (e & 3) (the S^T accumulator order), so
@@ -338,87 +360,121 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   // half's S^T products in flight during the first half's softmax.  The K operands of
   // the stage are read from LDS up front; each half's V operands just before its
   // softmax (holding all of them would cost the third wave per SIMD its registers).
-  auto compute_stage = [&](int buf, int k0) __attribute__((always_inline)) {
+  auto compute_stage_fast = [&](int buf, int k0) __attribute__((always_inline)) {
     KOps k0o, k1o;
     read_k(buf, 0, k0o);
     read_k(buf, 1, k1o);
-    uint32_t p0[8], p1[8];
+    uint32_t p0[8], p1[8], unused[8];
     const f32x16_t s0 = qk(k0o);
     const f32x16_t s1 = qk(k1o);
     {
       VOps v0o;
       read_v(buf, 0, v0o);
-      softmax(s0, k0, p0);
+      softmax(s0, k0, p0, unused, std::false_type{});
       pv(v0o, p0);
     }
     if (__builtin_expect(k0 + 32 < kend, 1)) {  // else masked whole: nothing to add
       VOps v1o;
       read_v(buf, 1, v1o);
-      softmax(s1, k0 + 32, p1);
+      softmax(s1, k0 + 32, p1, unused, std::false_type{});
       pv(v1o, p1);
     }
   };
-
-  // Stage pipeline (stage indices relative to st0).  At iteration st: LDS buffer st % 2
-  // holds stage st, the registers of stage st + 1 are in flight (issued an iteration
-  // ago), and the block-table entries of stage st + 2 have arrived.  The iteration issues
-  // the block-table loads of stage st + 3 and the K/V loads of stage st + 2, computes
-  // stage st from LDS, stores stage st + 1 to the other buffer and meets the barrier.
-  // Every load is issued unconditionally (stages past the end are the cheap `live =
-  // false` kind) and the loop is unrolled by two with fixed registers per parity, so the
-  // compiler's wait counts let the loads of stage st + 2 stay in flight across the store
-  // of stage st + 1.
-  StageRegs ra, rb;   // stage u lives in ra for even u, rb for odd u
-  int pa_e, pb_e, pa_o, pb_o;  // block-table entries for even / odd stages
-  if (n_stages > 0) {
-    int p0a, p0b;
-    stage_pids(st0, p0a, p0b);
-    stage_pids(st0 + 1, pa_o, pb_o);
-    stage_load(ra, p0a, p0b, true);
-    stage_pids(st0 + 2, pa_e, pb_e);
-    stage_load(rb, pa_o, pb_o, 1 < n_stages);
-    stage_store(ra, st0, 0);
-  }
-  // An explicit use of q here, after the prologue has waited for younger loads: the
-  // compiler's wait counts then know q has arrived on every path into the loop, instead
-  // of waiting for it (and every load issued after it) at the top of each trip.
-  asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
-  __syncthreads();
-  // One iteration for stage st of parity P (0: st even).  Registers are chosen by name at
-  // compile time (stage u lives in ra for even u, rb for odd u; the block-table entries of
-  // stage u in pa_e/pb_e or pa_o/pb_o by the parity of u) so nothing is addressed through
-  // a pointer and no register set spills to scratch.
-  auto iteration = [&](int st, auto parity) __attribute__((always_inline)) {
-    constexpr int P = decltype(parity)::value;
-    const int buf = st & 1;
-    // block-table entries of stage st + 3 (parity !P) ; K/V of stage st + 2 (parity P)
-    if constexpr (P == 0) {
-      stage_pids(st0 + st + 3, pa_o, pb_o);
-      stage_load(ra, pa_e, pb_e, st + 2 < n_stages);
-    } else {
-      stage_pids(st0 + st + 3, pa_e, pb_e);
-      stage_load(rb, pa_o, pb_o, st + 2 < n_stages);
+  // The same for a tile with rows that see few keys: the halves one after the other (so
+  // the remainders' registers fit where the second half's scores sat), P.V over the hi
+  // terms, then over the lo terms.
+  auto compute_stage_precise = [&](int buf, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (hh == 0 || k0 + 32 < kend) {
+        KOps ko;
+        read_k(buf, hh, ko);
+        const f32x16_t sh_ = qk(ko);
+        VOps vo;
+        read_v(buf, hh, vo);
+        uint32_t ph[8], pl[8];
+        softmax(sh_, k0 + 32 * hh, ph, pl, std::true_type{});
+        pv(vo, ph);
+        pv(vo, pl);
+      }
     }
-    compute_stage(buf, (st0 + st) * kStage);
-    // Stored on every iteration, also past the last stage (the other buffer is not read
-    // again then): a store skipped on some paths would leave its loads pending at the loop
-    // back edge, and the compiler then waits for every load at the top of the loop.
-    if constexpr (P == 0)
-      stage_store(rb, st0 + st + 1, buf ^ 1);
-    else
-      stage_store(ra, st0 + st + 1, buf ^ 1);
-    __syncthreads();
   };
-  // Pairs of stages, then an odd last stage alone: the loop has a single back edge and
-  // one exit, so the compiler's wait at the loop top covers only the block-table entries,
-  // not the K/V loads meant to stay in flight (an exit between the two halves made it
-  // wait for every load there).  The odd last stage has nothing left to load or store.
-  int st = 0;
-  for (; st + 1 < n_stages; st += 2) {
-    iteration(st, std::integral_constant<int, 0>{});
-    iteration(st + 1, std::integral_constant<int, 1>{});
+
+  if (__builtin_expect(precise, 0)) {
+    // A tile with rows that see few keys has at most two stages (causal: its keys end
+    // within 32 of its first row, which sits below 63; otherwise the context is shorter
+    // than a stage): staged one at a time, without the pipeline.
+    for (int st = 0; st < n_stages; ++st) {
+      int pa_s, pb_s;
+      stage_pids(st0 + st, pa_s, pb_s);
+      StageRegs r;
+      stage_load(r, pa_s, pb_s, true);
+      stage_store(r, st0 + st, st & 1);
+      __syncthreads();
+      compute_stage_precise(st & 1, (st0 + st) * kStage);
+    }
+  } else {
+    // Stage pipeline (stage indices relative to st0).  At iteration st: LDS buffer st % 2
+    // holds stage st, the registers of stage st + 1 are in flight (issued an iteration
+    // ago), and the block-table entries of stage st + 2 have arrived.  The iteration issues
+    // the block-table loads of stage st + 3 and the K/V loads of stage st + 2, computes
+    // stage st from LDS, stores stage st + 1 to the other buffer and meets the barrier.
+    // Every load is issued unconditionally (stages past the end are the cheap `live =
+    // false` kind) and the loop is unrolled by two with fixed registers per parity, so the
+    // compiler's wait counts let the loads of stage st + 2 stay in flight across the store
+    // of stage st + 1.
+    StageRegs ra, rb;   // stage u lives in ra for even u, rb for odd u
+    int pa_e, pb_e, pa_o, pb_o;  // block-table entries for even / odd stages
+    if (n_stages > 0) {
+      int p0a, p0b;
+      stage_pids(st0, p0a, p0b);
+      stage_pids(st0 + 1, pa_o, pb_o);
+      stage_load(ra, p0a, p0b, true);
+      stage_pids(st0 + 2, pa_e, pb_e);
+      stage_load(rb, pa_o, pb_o, 1 < n_stages);
+      stage_store(ra, st0, 0);
+    }
+    // An explicit use of q here, after the prologue has waited for younger loads: the
+    // compiler's wait counts then know q has arrived on every path into the loop, instead
+    // of waiting for it (and every load issued after it) at the top of each trip.
+    asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
+    __syncthreads();
+    // One iteration for stage st of parity P (0: st even).  Registers are chosen by name at
+    // compile time (stage u lives in ra for even u, rb for odd u; the block-table entries of
+    // stage u in pa_e/pb_e or pa_o/pb_o by the parity of u) so nothing is addressed through
+    // a pointer and no register set spills to scratch.
+    auto iteration = [&](int st, auto parity) __attribute__((always_inline)) {
+      constexpr int P = decltype(parity)::value;
+      const int buf = st & 1;
+      // block-table entries of stage st + 3 (parity !P) ; K/V of stage st + 2 (parity P)
+      if constexpr (P == 0) {
+        stage_pids(st0 + st + 3, pa_o, pb_o);
+        stage_load(ra, pa_e, pb_e, st + 2 < n_stages);
+      } else {
+        stage_pids(st0 + st + 3, pa_e, pb_e);
+        stage_load(rb, pa_o, pb_o, st + 2 < n_stages);
+      }
+      compute_stage_fast(buf, (st0 + st) * kStage);
+      // Stored on every iteration, also past the last stage (the other buffer is not read
+      // again then): a store skipped on some paths would leave its loads pending at the loop
+      // back edge, and the compiler then waits for every load at the top of the loop.
+      if constexpr (P == 0)
+        stage_store(rb, st0 + st + 1, buf ^ 1);
+      else
+        stage_store(ra, st0 + st + 1, buf ^ 1);
+      __syncthreads();
+    };
+    // Pairs of stages, then an odd last stage alone: the loop has a single back edge and
+    // one exit, so the compiler's wait at the loop top covers only the block-table entries,
+    // not the K/V loads meant to stay in flight (an exit between the two halves made it
+    // wait for every load there).  The odd last stage has nothing left to load or store.
+    int st = 0;
+    for (; st + 1 < n_stages; st += 2) {
+      iteration(st, std::integral_constant<int, 0>{});
+      iteration(st + 1, std::integral_constant<int, 1>{});
+    }
+    if (st < n_stages) compute_stage_fast(st & 1, (st0 + st) * kStage);
   }
-  if (st < n_stages) compute_stage(st & 1, (st0 + st) * kStage);
 
   if (n_split > 1) {
     // a piece: fp32 partial (reference maximum, sum, unnormalised output) for the merge,

@@ -11,6 +11,55 @@ import oracle as O
 import workloads as W
 
 
+# The parity bar: max-abs 1e-2 and mean-abs 1e-3 of the bf16 output widened to fp32
+# against the fp64 oracle rounded to fp32, over all elements of a case.
+MAX_ABS = 1e-2
+MEAN_ABS = 1e-3
+# At |o| >= 4 two neighbouring bf16 values lie 2^-5 apart, so even the correctly rounded
+# output can miss the exact value by 2^-6 > MAX_ABS.  Such elements are held to half a
+# bf16 unit of the exact value plus R13_SLACK (the kernels' fp32 arithmetic can put a
+# value within that of a rounding midpoint on the other side) and are counted.
+R13_ABS = 4.0
+R13_SLACK = 1e-3
+
+
+def bf16_half_unit(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of bf16 values around |x| (8 significant bits): 2^(e - 8) for
+    |x| in [2^e, 2^(e+1))."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, (np.floor(np.log2(ax)) - 8).astype(np.int64))
+
+
+def parity_stats(gpu_f32: np.ndarray, ref_f64: np.ndarray) -> dict:
+    """Element-wise comparison at the parity bar.  Returns max-abs and mean-abs over all
+    elements, the counts of elements with |oracle| >= 2 and >= R13_ABS, the largest error
+    among elements below R13_ABS, and whether every element meets its bar (MAX_ABS below
+    R13_ABS, half a bf16 unit + R13_SLACK at or above it) and mean-abs <= MEAN_ABS."""
+    g = np.asarray(gpu_f32, dtype=np.float32).reshape(-1)
+    r = np.asarray(ref_f64, dtype=np.float64).astype(np.float32).reshape(-1)
+    diff = np.abs(g.astype(np.float64) - r.astype(np.float64))
+    big = np.abs(r) >= R13_ABS
+    bar = np.where(big, bf16_half_unit(r) + R13_SLACK, MAX_ABS)
+    excess = diff - bar
+    n = diff.size
+    st = {
+        "n": int(n),
+        "finite": bool(np.isfinite(g).all()),
+        "max_abs": float(diff.max()) if n else 0.0,
+        "mean_abs": float(diff.mean()) if n else 0.0,
+        "max_abs_below_r13": float(diff[~big].max()) if (~big).any() else 0.0,
+        "n_abs_ge_2": int((np.abs(r) >= 2.0).sum()),
+        "n_abs_ge_4": int(big.sum()),
+        "n_r13_over_max_abs": int((diff[big] > MAX_ABS).sum()),
+        "worst_excess": float(excess.max()) if n else 0.0,
+    }
+    if n:
+        i = int(np.argmax(excess))
+        st["worst"] = {"index": i, "gpu": float(g[i]), "oracle": float(r[i]), "err": float(diff[i])}
+    st["ok"] = bool(st["finite"] and (excess <= 0).all() and st["mean_abs"] <= MEAN_ABS)
+    return st
+
+
 def oracle_pools(case: W.Case):
     """Pools (K, V) as the oracle's own kv_append writes them: sentinel everywhere,
     then the setup tokens, then the step's new tokens."""

@@ -93,3 +93,100 @@ def test_decode_append_long_contexts_sampled():
     _announce("decode_append workload 4")
     a, b, same, out_b, _ = _both_paths(case, 0)
     assert np.array_equal(a, b) and same
+
+
+def test_decode_append_past_max_ctx_writes_nothing():
+    """A sequence whose length exceeds max_ctx_len: its new row is not written (the pools
+    equal the oracle's with that row left out), its output is NaN, and every other
+    sequence is appended and attended as usual."""
+    import torch
+
+    import oracle as O
+    import paged_kv_attention_31_amd as pa
+
+    ctx = [40, 300, 7, 129]
+    case = W.custom_case(ctx, [1] * 4, block_size=16, seed=102)
+    _announce("decode_append with a sequence past max_ctx_len")
+    geom = geometry(case)
+    hkv, d, n = case.num_kv_heads, case.head_dim, case.n_seqs
+    kp, vp = sentinel_pools(case)
+    bt = i32_dev(case.block_tables)
+    pa.kv_append(geom, bf16_dev(case.k_setup), bf16_dev(case.v_setup), kp, vp, bt,
+                 i32_dev(case.cu_setup_lens), i32_dev(case.setup_ctx_lens))
+    out = torch.empty((n, 32, 64), dtype=torch.bfloat16, device="cuda:0")
+    pa.decode_append(geom, out, bf16_dev(case.q_decode), bf16_dev(case.k_new.reshape(n, hkv, d)),
+                     bf16_dev(case.v_new.reshape(n, hkv, d)), kp, vp, bt, i32_dev(case.ctx_lens),
+                     200, case.scale)
+    torch.cuda.synchronize()
+    keep = [0, 2, 3]
+    kpo, vpo = W.sentinel_pool(case), W.sentinel_pool(case)
+    O.kv_append(kpo, vpo, case.k_setup, case.v_setup, case.block_tables, case.cu_setup_lens,
+                case.setup_ctx_lens, case.block_size)
+    rows = [int(case.cu_new_lens[s]) for s in keep]
+    O.kv_append(kpo, vpo, case.k_new[rows], case.v_new[rows], case.block_tables[keep],
+                np.arange(len(keep) + 1, dtype=np.int32), case.ctx_lens[keep], case.block_size)
+    assert np.array_equal(bits_host(kp), kpo) and np.array_equal(bits_host(vp), vpo)
+    host = out.float().cpu().numpy()
+    assert np.all(np.isnan(host[1]))
+    kp_o, vp_o = oracle_pools(case)
+    ref = oracle_decode(case, kp_o, vp_o, seqs=keep)
+    assert_close(out[keep], ref[keep], "sequences within max_ctx_len")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_on_a_side_stream_with_its_own_workspace(fused):
+    """A call on a stream other than the current one, with no workspace given.  The
+    binding's workspace is recorded on that stream: while the stream still has work
+    queued, a block freed from it is not handed to an allocation on the current stream
+    (checked on the binding's allocator helper directly); and the call's output, with
+    the current stream allocating and writing scratch of the same size meanwhile,
+    matches the oracle."""
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    case = W.custom_case([700, 1, 3000, 65, 129, 2049], [1] * 6, block_size=32, seed=103)
+    _announce(f"decode on a side stream (fused={fused})")
+    geom = geometry(case)
+    hkv, d, n = case.num_kv_heads, case.head_dim, case.n_seqs
+    kp, vp = sentinel_pools(case)
+    bt = i32_dev(case.block_tables)
+    pa.kv_append(geom, bf16_dev(case.k_setup), bf16_dev(case.v_setup), kp, vp, bt,
+                 i32_dev(case.cu_setup_lens), i32_dev(case.setup_ctx_lens))
+    ctx = i32_dev(case.ctx_lens)
+    q = bf16_dev(case.q_decode)
+    k_new = bf16_dev(case.k_new.reshape(n, hkv, d))
+    v_new = bf16_dev(case.v_new.reshape(n, hkv, d))
+    if not fused:
+        pa.kv_append(geom, k_new, v_new, kp, vp, bt, i32_dev(np.arange(n + 1, dtype=np.int32)),
+                     ctx)
+    mc, part = int(case.ctx_lens.max()), 64
+    need = pa.decode_workspace_bytes(geom, n, mc, part)
+    assert need > 0
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    dev = torch.device("cuda:0")
+    # the mechanism: a block recorded on a busy side stream is not reused at once
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+    ws = pa._scratch(need, dev, side)
+    ptr = ws.data_ptr()
+    del ws
+    fresh = torch.empty(need, dtype=torch.uint8, device=dev)
+    assert fresh.data_ptr() != ptr
+    del fresh
+    # the call itself, behind a spin on the side stream
+    out = torch.empty((n, 32, 64), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)
+    if fused:
+        pa.decode_append(geom, out, q, k_new, v_new, kp, vp, bt, ctx, mc, case.scale,
+                         partition_tokens=part, stream=side)
+    else:
+        pa.decode(geom, out, q, kp, vp, bt, ctx, mc, case.scale, partition_tokens=part,
+                  stream=side)
+    junk = [torch.full((need,), 255, dtype=torch.uint8, device=dev) for _ in range(4)]
+    torch.cuda.synchronize()
+    del junk
+    kp_o, vp_o = oracle_pools(case)
+    assert_close(out, oracle_decode(case, kp_o, vp_o), f"side stream fused={fused}")

@@ -7,12 +7,10 @@ pa_decode_append (append and attention in one launch).  One run appends through 
 instead: then Q and every cached K are turned by their positions (oracle: the rotation in
 fp64, rounded once to bf16), so the plans' positions are checked as well.
 
-Tolerance: the parity bar's mean-abs (1e-3) over the run, and per element its max-abs
-bar widened by one bf16 rounding of the result, |gpu - oracle| <= 1e-2 + 2^-8 |oracle|.
-The widening matters only for rows that see a handful of keys (the first rows of every
-prompt; here prompts start at 1 token), whose outputs are single V values of size up to
-~4, where one bf16 unit is 2^-6 and the kernel's bf16 probabilities and bf16 output each
-round by up to half of that."""
+Tolerance: the parity bar, element by element over the whole run (max-abs 1e-2, mean-abs
+1e-3; elements with |oracle| >= 4, where half a bf16 unit exceeds 1e-2, are held to half a
+bf16 unit and counted).  The first rows of every prompt (prompts start at 1 token) see a
+handful of keys, the case in which the kernels' two-term probabilities matter."""
 
 from __future__ import annotations
 
@@ -21,7 +19,8 @@ import pytest
 
 import oracle as O
 import workloads as W
-from tests.gpu_helpers import MAX_ABS, MEAN_ABS, bf16_dev, f32_host, i32_dev
+from tests.gpu_helpers import bf16_dev, f32_host, i32_dev
+from tests.helpers import parity_stats
 
 pytestmark = pytest.mark.gpu
 
@@ -125,15 +124,12 @@ def test_scheduler_plans_drive_the_kernels(bs, slots, chunk, rope, fused):
     assert produced == {rid: r["max_new"] for rid, r in reqs.items()}
     assert pa.STEP_PREFILL in kinds and pa.STEP_DECODE in kinds
     g = np.concatenate([x.reshape(-1) for x in gpu_rows]).astype(np.float32)
-    r = np.concatenate([x.reshape(-1) for x in ref_rows]).astype(np.float32)
-    diff = np.abs(g - r).astype(np.float64)
-    assert np.all(np.isfinite(g))
-    excess = diff - (MAX_ABS + 2.0 ** -8 * np.abs(r))
-    worst = int(np.argmax(excess))
-    assert excess[worst] <= 0 and diff.mean() <= MEAN_ABS, (
-        f"max-abs {diff.max():.4g}, worst element {worst}: gpu {g[worst]:.6g} oracle "
-        f"{r[worst]:.6g}; mean-abs {diff.mean():.3g}")
-    _announce(f"max-abs {diff.max():.4g} (at oracle value {r[int(np.argmax(diff))]:.4g}), "
-              f"mean-abs {diff.mean():.3g}")
+    r = np.concatenate([x.reshape(-1) for x in ref_rows])
+    st = parity_stats(g, r)
+    _announce(f"max-abs {st['max_abs']:.4g} (below |o|=4: {st['max_abs_below_r13']:.4g}), "
+              f"mean-abs {st['mean_abs']:.3g}; |o|>=2: {st['n_abs_ge_2']}, |o|>=4: "
+              f"{st['n_abs_ge_4']} ({st['n_r13_over_max_abs']} beyond 1e-2) of {st['n']}")
+    assert st["finite"]
+    assert st["ok"], f"parity: {st}"
     sched.close()
     assert pool.num_free() == num_pages
