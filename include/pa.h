@@ -294,6 +294,25 @@ int pa_decode_append(pa_geom_t g, void* out, const void* q, const void* k_new,
                      void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * decode_noalloc: pa_decode for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments,
+ * outputs and errors are those of pa_decode without the workspace: the split-K partials
+ * go to a device array of the library's own, PA_DECODE_SCRATCH_BYTES per device, held
+ * until the process ends.  The call allocates and frees nothing.  It returns
+ * PA_ERR_WORKSPACE, before any launch, when pa_decode_workspace_bytes(...) for the same
+ * arguments exceeds PA_DECODE_SCRATCH_BYTES (with the automatic partition on MI355X that
+ * is about n_seqs * num_kv_heads + 1024 > 15800, e.g. more than 1900 sequences at 8 KV
+ * heads once any context exceeds 64 tokens).  The scratch needs no initialisation.  Every
+ * call on one device shares that device's array: calls that overlap in time on one
+ * device (other streams, other threads) race on it and must be serialised by the caller.
+ * ------------------------------------------------------------------------------- */
+#define PA_DECODE_SCRATCH_BYTES (16u << 20)
+int pa_decode_noalloc(pa_geom_t g, void* out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* ctx_lens, int32_t n_seqs, int32_t max_ctx_len, float scale,
+                      int32_t partition_tokens, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Prefill, whole prompts or chunks ([guide] §推理流程: prefill handles every prompt
  * token in parallel; [实战] §算子融合: tiled attention with online softmax never
  * materialises the seq x seq score matrix).  Query rows are packed by sequence: rows

@@ -27,6 +27,7 @@ __all__ = [
     "STEP_PREFILL", "STEP_DECODE", "page_bytes", "kv_append", "rope_kv_append",
     "copy_pages", "residual_rmsnorm", "silu_mul",
     "decode_partition_tokens", "decode_workspace_bytes", "decode", "decode_append",
+    "decode_noalloc", "DECODE_SCRATCH_BYTES",
     "prefill_workspace_bytes",
     "prefill", "library",
 ]
@@ -430,6 +431,33 @@ def decode_append(geom: Geometry, out, q, k_new, v_new, k_pool, v_pool, block_ta
         _ptr(block_tables), int(block_tables.shape[1]), _ptr(ctx_lens), n, int(max_ctx_len),
         float(scale), int(partition_tokens), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "pa_decode_append")
+
+
+DECODE_SCRATCH_BYTES = _lib.PA_DECODE_SCRATCH_BYTES
+
+
+def decode_noalloc(geom: Geometry, out, q, k_pool, v_pool, block_tables, ctx_lens,
+                   max_ctx_len: int, scale: float, partition_tokens: int = 0,
+                   stream=None) -> None:
+    """pa_decode without a workspace (see pa_decode_noalloc): the split-K partials go to
+    the library's own device scratch of DECODE_SCRATCH_BYTES, so nothing is allocated.
+    Calls that overlap on one device share that scratch and must be serialised."""
+    import torch
+
+    n = int(ctx_lens.numel())
+    rows = n * geom.num_q_heads * geom.head_dim
+    _dev(out, "out", torch.bfloat16, rows)
+    _dev(q, "q", torch.bfloat16, rows)
+    for name, x in (("k_pool", k_pool), ("v_pool", v_pool)):
+        _dev(x, name, torch.bfloat16, geom.num_pages * geom.page_elems)
+    _dev(block_tables, "block_tables", torch.int32, dims=2)
+    _dev(ctx_lens, "ctx_lens", torch.int32, n)
+    _need(block_tables.shape[0] == n, "block_tables rows != n_seqs")
+    st = _lib.load().pa_decode_noalloc(geom.c(), _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                       _ptr(block_tables), int(block_tables.shape[1]),
+                                       _ptr(ctx_lens), n, int(max_ctx_len), float(scale),
+                                       int(partition_tokens), _stream(stream))
+    _check(st, "pa_decode_noalloc")
 
 
 def prefill_workspace_bytes(geom: Geometry, n_seqs: int, max_q_len: int, max_ctx_len: int,

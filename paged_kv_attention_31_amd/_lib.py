@@ -38,6 +38,7 @@ class PaSchedStep(ctypes.Structure):
 
 
 PA_STEP_IDLE, PA_STEP_PREFILL, PA_STEP_DECODE = 0, 1, 2
+PA_DECODE_SCRATCH_BYTES = 16 << 20  # pa_decode_noalloc's device scratch per device
 
 _c_i32 = ctypes.c_int32
 _c_p = ctypes.c_void_p
@@ -83,6 +84,8 @@ SIGNATURES = {
     "pa_decode_append": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                         _c_i32, _c_p, _c_i32, _c_i32, ctypes.c_float, _c_i32,
                                         _c_p, ctypes.c_size_t, _c_p]),
+    "pa_decode_noalloc": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p,
+                                         _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_p]),
     "pa_prefill_workspace_bytes": (ctypes.c_size_t, [PaGeom, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_prefill": (ctypes.c_int, [PaGeom, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_p,
                                   _c_i32, _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_i32, _c_p,

@@ -362,6 +362,30 @@ int pa_decode_append(pa_geom_t g, void* out, const void* q, const void* k_new,
                                       workspace, static_cast<hipStream_t>(stream), k_new, v_new));
 }
 
+int pa_decode_noalloc(pa_geom_t g, void* out, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* ctx_lens, int32_t n_seqs, int32_t max_ctx_len, float scale,
+                      int32_t partition_tokens, void* stream) {
+  const int st = decode_args_ok(g, n_seqs, max_ctx_len, partition_tokens);
+  if (st != PA_OK) return st;
+  if (max_blocks_per_seq <= 0) return PA_ERR_INVALID_ARG;
+  if ((int64_t)max_ctx_len > (int64_t)max_blocks_per_seq * g.block_size) return PA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PA_ERR_INVALID_ARG;
+  if (n_seqs == 0) return PA_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !ctx_lens) return PA_ERR_INVALID_ARG;
+  const pa::DecodePlan plan = pa::plan_decode(n_seqs, max_ctx_len, g.num_kv_heads,
+                                              partition_tokens, compute_units());
+  if (plan.ws_bytes > (size_t)PA_DECODE_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    const hipError_t e = pa::decode_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(pa::launch_decode(to_launch(g), plan, out, q, k_pool, v_pool, block_tables,
+                                      max_blocks_per_seq, ctx_lens, n_seqs, max_ctx_len, scale,
+                                      ws, static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_prefill_workspace_bytes(pa_geom_t g, int32_t n_seqs, int32_t max_q_len,
                                   int32_t max_ctx_len, int32_t kv_splits) {
   if (prefill_args_ok(g, n_seqs, max_q_len, max_ctx_len, kv_splits) != PA_OK) return 0;

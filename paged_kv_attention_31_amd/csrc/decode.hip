@@ -39,11 +39,36 @@
 // combines them by log-sum-exp in ascending wave order (a fixed order: results do not
 // depend on scheduling).
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
 
+// Split-K scratch of pa_decode_noalloc: a device array of the library's own, so that call
+// allocates nothing.  Each device holds its own copy until the process ends; host code
+// reaches it only through the address hipGetSymbolAddress gives on that device.
+static __device__ __align__(256) unsigned char scratch[PA_DECODE_SCRATCH_BYTES];
+
 namespace pa {
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {  // once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

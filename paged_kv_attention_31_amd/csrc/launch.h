@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
 
 constexpr int kHeadDim = 64;  // head_dim the kernels are built for
@@ -67,6 +69,10 @@ struct DecodePlan {
 // more than partition_tokens tokens (a multiple of 64).
 DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partition_tokens,
                        int compute_units);
+
+// Device address of the library's own split-K scratch (PA_DECODE_SCRATCH_BYTES) on the
+// current device, looked up once per device.
+hipError_t decode_scratch(void** ptr);
 
 hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* out, const void* q,
                          const void* k_pool, const void* v_pool, const int32_t* block_tables,

@@ -167,6 +167,32 @@ def test_decode_append_validation_returns_before_launch(lib):
                           part=256) == _lib.PA_ERR_WORKSPACE
 
 
+def _decode_noalloc(lib, g=None, out=FAKE, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, max_blocks=4,
+                    ctx=FAKE, n=2, max_ctx=64, scale=0.125, part=0):
+    return lib.pa_decode_noalloc(g or geom(), out, q, kp, vp, bt, max_blocks, ctx, n, max_ctx,
+                                 scale, part, None)
+
+
+def test_decode_noalloc_validation_and_scratch_limit(lib):
+    """pa_decode_noalloc checks what pa_decode checks, and refuses, before any launch, a
+    call whose split-K partials exceed its fixed device scratch."""
+    for missing in ("out", "q", "kp", "vp", "bt", "ctx"):
+        assert _decode_noalloc(lib, **{missing: None}) == _lib.PA_ERR_INVALID_ARG, missing
+    assert _decode_noalloc(lib, g=geom(d=128)) == _lib.PA_ERR_UNSUPPORTED
+    assert _decode_noalloc(lib, max_ctx=65) == _lib.PA_ERR_INVALID_ARG
+    assert _decode_noalloc(lib, part=100) == _lib.PA_ERR_INVALID_ARG
+    assert _decode_noalloc(lib, scale=float("nan")) == _lib.PA_ERR_INVALID_ARG
+    assert _decode_noalloc(lib, n=0, out=None) == 0
+    assert _lib.PA_DECODE_SCRATCH_BYTES == 16 << 20
+    # the largest batch that fits, and the first that does not (contexts of 2 tiles)
+    g = geom(num_pages=4096)
+    fits = [n for n in range(1000, 3000, 10)
+            if _plan_ws(n, 128, 8, 0) <= _lib.PA_DECODE_SCRATCH_BYTES]
+    n_big = max(fits) + 10
+    assert lib.pa_decode_workspace_bytes(g, n_big, 128, 0) > _lib.PA_DECODE_SCRATCH_BYTES
+    assert _decode_noalloc(lib, g=g, n=n_big, max_blocks=8, max_ctx=128) == _lib.PA_ERR_WORKSPACE
+
+
 def _plan_ws(n_seqs, max_ctx, hkv, part, cus=256):
     """Workspace bytes of the documented decode plan (no device here: 256 compute units)."""
     tiles = max(1, -(-max_ctx // 64))
