@@ -324,6 +324,23 @@ class HeadStart:
             self.torch.cuda._sleep(self.cycles)
 
 
+def prefill_roofline(res: dict, base: W.Case, traffic_key: str) -> dict:
+    """pa_prefill against dense bf16 MFMA peak, and the least HBM traffic the launch needs
+    (q and out once, each sequence's K/V once) at the measured time against HBM peak: the
+    other bound a prefill launch is near."""
+    ach = res["prefill_tflops"]
+    min_b = prefill_min_bytes(base)
+    gbps = min_b / (res["prefill_ms"] * 1e-3) / 1e9
+    return {"bound": "mfma",
+            "kernel": "pa_prefill (prefill_kernel [+ prefill_merge_kernel when split])",
+            "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": hbm_traffic(traffic_key),
+            "flop_per_launch": res["prefill_flop_per_launch"],
+            "avg_launch_ms": round(res["prefill_ms"], 5),
+            "hbm_min_bytes": min_b, "hbm_min_gbps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     import torch
 
@@ -633,6 +650,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixed", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill-target", action="store_true",
+                    help="mixed workload: skip the 8-prompt prefill measurement")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--partition", type=int, default=0,
                     help="decode KV tokens per split-K partition (0 = the library's choice)")
@@ -720,22 +739,17 @@ def main() -> int:
         else:
             line["roofline"] = dec_line
     if "prefill_ms" in res:
-        ach = res["prefill_tflops"]
         key = "roofline_prefill" if "roofline" in line else "roofline"
-        line[key] = {"bound": "mfma", "kernel": "pa_prefill (prefill_kernel [+ prefill_merge_kernel when split])",
-                     "achieved": round(ach, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": hbm_traffic(args.workload + "-prefill" if key == "roofline_prefill"
-                                            else args.workload),
-                     "flop_per_launch": res["prefill_flop_per_launch"],
-                     "avg_launch_ms": round(res["prefill_ms"], 5)}
-        # the least HBM traffic a prefill launch needs (q and out once, each sequence's K/V
-        # once) at the measured time, against HBM peak: the other bound this launch is near
-        min_b = prefill_min_bytes(base)
-        gbps = min_b / (res["prefill_ms"] * 1e-3) / 1e9
-        line[key].update(hbm_min_bytes=min_b, hbm_min_gbps=round(gbps, 1),
-                         hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
+        line[key] = prefill_roofline(res, base, args.workload + "-prefill"
+                                     if key == "roofline_prefill" else args.workload)
+    if args.workload == "mixed" and not args.no_prefill_target:
+        # the prefill target's own workload (8 whole prompts), measured in the same run
+        log("prefill workload (8 prompts) for the prefill roofline")
+        res3 = run_gpu(3, args.steps, args.warmup)
+        base3 = W.make_case(3, values=False)
+        line["roofline_prefill_8prompts"] = dict(
+            {"workload": W.CONFIG_NAMES[3], "layer_copies": res3["n_layers"]},
+            **prefill_roofline(res3, base3, "prefill"))
     line["append_ms_per_layer"] = round(res["append_ms"], 5)
     line["cpu_baseline"] = dict(cpu, **host_cpu()) if cpu else cpu
     print(json.dumps(line), flush=True)

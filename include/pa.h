@@ -320,19 +320,22 @@ int pa_decode_noalloc(pa_geom_t g, void* out, const void* q, const void* k_pool,
  * ctx_lens[s] - q_len_s + i and sees keys 0..position (causal != 0) or all
  * ctx_lens[s] keys (causal == 0).  Keys before the chunk come from earlier appends,
  * so a chunk attends to the cached prefix.  Matrix products run on bf16 MFMA with fp32
- * accumulation.  One workgroup per (tile of 32 query rows, sequence, KV head); when the
- * call has fewer such tiles than two per compute unit, each tile's keys are split into
- * pieces whose fp32 partials (max, sum, unnormalised output) a second kernel merges by
- * log-sum-exp in piece order.
+ * accumulation.  One workgroup per (tile of 32 query rows, sequence, KV head).  When the
+ * call has fewer tiles than compute units, a workgroup runs two groups of four waves that
+ * take alternate 64-key stages of its tile and merge their results in LDS.  When the
+ * grid is still small, each tile's keys are also split into pieces whose fp32 partials
+ * (max, sum, unnormalised output) a second kernel merges by log-sum-exp in piece order.
  *   out, q      [n_q_tokens][num_q_heads][head_dim] bf16 (device),
  *               n_q_tokens = cu_q_lens[n_seqs]
  *   cu_q_lens   int32 [n_seqs+1] (device); q_len_s <= ctx_lens[s] required
  *   max_q_len   host upper bound of q_len_s (sizes the grid: rows past it are not written)
  *   max_ctx_len host upper bound of ctx_lens (<= max_blocks_per_seq * block_size)
  *   scale       as for pa_decode: finite and > 0
- *   kv_splits   0: automatic (1 when the grid has at least two tiles per compute unit of
- *               the current device, else enough pieces for that, at most 8 and at most
- *               ceil(max_ctx_len/64)); else that many pieces, 1 .. 8.  Other values give
+ *   kv_splits   0: automatic, from the T tiles below and the C compute units of the
+ *               current device: with T >= C, enough pieces for 2 C workgroups; with
+ *               T < C (two key groups per workgroup), enough for C / 2 workgroups; 1 when
+ *               T already reaches that, and always at most 8 and at most
+ *               ceil(max_ctx_len/64).  Else that many pieces, 1 .. 8.  Other values give
  *               PA_ERR_INVALID_ARG.
  *   workspace   device scratch of at least pa_prefill_workspace_bytes(...) bytes for the
  *               same arguments (on the same device); may be NULL when that size is 0.

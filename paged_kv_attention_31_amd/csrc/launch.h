@@ -80,14 +80,17 @@ hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* ou
                          float scale, void* workspace, hipStream_t stream,
                          const void* k_new = nullptr, const void* v_new = nullptr);
 
-// Prefill: one workgroup per (query tile of 32, sequence, KV head); when that gives fewer
-// than two workgroups per compute unit the tile's keys are split into up to
-// kPrefillMaxSplit pieces whose fp32 partials a merge kernel combines.
+// Prefill: one workgroup per (query tile of 32, sequence, KV head).  With fewer tiles than
+// compute units a workgroup holds two key groups of four waves that take alternate key
+// stages of its tile and merge in LDS; with still too few workgroups (or fewer than two
+// per compute unit) the tile's keys are also split into up to kPrefillMaxSplit pieces
+// whose fp32 partials a merge kernel combines.
 constexpr int kPrefillMaxSplit = 8;
 
 struct PrefillPlan {
   int64_t items;    // tiles x sequences x KV heads (the tile grid, ceil(max_q/32) tiles each)
   int split;        // key pieces per tile (1: no merge)
+  int groups;       // key groups per workgroup (1 or 2)
   size_t ws_bytes;  // partials (0 when split is 1)
 };
 

@@ -82,8 +82,8 @@ struct PrefillLds {
   uint16_t v[2][PPS][kHeadDim][VROW];      // [stage][page][dim][bs + pad]
 };
 
-template <int BS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void prefill_kernel(
+template <int BS, int G>
+__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks,
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   constexpr int PPS = Lds::PPS;
   constexpr int VROW = Lds::VROW;
   constexpr int KCH = 8 * BS;  // 16-byte chunks of one page's K (or V) head slice
-  __shared__ __attribute__((aligned(16))) Lds sh;
+  __shared__ __attribute__((aligned(16))) Lds sh_all[G];
 
   // Work order: tiles longest first (highest query positions see the most keys), the
   // sequences of one tile level rotated by the level.  The hardware hands workgroups to
@@ -110,7 +110,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
   const int level = tb / n_seqs;
   const int s = (tb % n_seqs + level) % n_seqs;
   const int tile = n_qtiles - 1 - level;
-  const int tid = threadIdx.x;
+  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);  // key group
+  Lds& sh = sh_all[grp];
+  const int tid = threadIdx.x & 255;  // thread within the group
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int j = lane & 31;    // query column of this lane
@@ -400,80 +402,124 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void p
     }
   };
 
+  // Key groups: group grp takes the piece's stages grp, grp + G, grp + 2G, ... (round u
+  // holds stage grp + G u of every group); every group runs the same number of rounds, so
+  // the workgroup barriers match, and a stage past the piece is loaded the cheap way and
+  // not computed.
+  const int n_u = (n_stages + G - 1) / G;
+  auto stage_of = [&](int u) __attribute__((always_inline)) { return st0 + grp + G * u; };
+  auto live_of = [&](int u) __attribute__((always_inline)) { return grp + G * u < n_stages; };
   if (__builtin_expect(precise, 0)) {
     // A tile with rows that see few keys has at most two stages (causal: its keys end
     // within 32 of its first row, which sits below 63; otherwise the context is shorter
     // than a stage): staged one at a time, without the pipeline.
-    for (int st = 0; st < n_stages; ++st) {
+    for (int u = 0; u < n_u; ++u) {
       int pa_s, pb_s;
-      stage_pids(st0 + st, pa_s, pb_s);
+      stage_pids(stage_of(u), pa_s, pb_s);
       StageRegs r;
-      stage_load(r, pa_s, pb_s, true);
-      stage_store(r, st0 + st, st & 1);
+      stage_load(r, pa_s, pb_s, live_of(u));
+      stage_store(r, stage_of(u), u & 1);
       __syncthreads();
-      compute_stage_precise(st & 1, (st0 + st) * kStage);
+      if (live_of(u)) compute_stage_precise(u & 1, stage_of(u) * kStage);
     }
   } else {
-    // Stage pipeline (stage indices relative to st0).  At iteration st: LDS buffer st % 2
-    // holds stage st, the registers of stage st + 1 are in flight (issued an iteration
-    // ago), and the block-table entries of stage st + 2 have arrived.  The iteration issues
-    // the block-table loads of stage st + 3 and the K/V loads of stage st + 2, computes
-    // stage st from LDS, stores stage st + 1 to the other buffer and meets the barrier.
-    // Every load is issued unconditionally (stages past the end are the cheap `live =
-    // false` kind) and the loop is unrolled by two with fixed registers per parity, so the
-    // compiler's wait counts let the loads of stage st + 2 stay in flight across the store
-    // of stage st + 1.
-    StageRegs ra, rb;   // stage u lives in ra for even u, rb for odd u
-    int pa_e, pb_e, pa_o, pb_o;  // block-table entries for even / odd stages
-    if (n_stages > 0) {
+    // Stage pipeline (in rounds).  At round u: LDS buffer u % 2 holds the group's stage of
+    // round u, the registers of round u + 1 are in flight (issued a round ago), and the
+    // block-table entries of round u + 2 have arrived.  The round issues the block-table
+    // loads of round u + 3 and the K/V loads of round u + 2, computes round u from LDS,
+    // stores round u + 1 to the other buffer and meets the barrier.  Every load is issued
+    // unconditionally (stages past the end are the cheap `live = false` kind) and the loop
+    // is unrolled by two with fixed registers per parity, so the compiler's wait counts let
+    // the loads of round u + 2 stay in flight across the store of round u + 1.
+    StageRegs ra, rb;   // round u lives in ra for even u, rb for odd u
+    int pa_e, pb_e, pa_o, pb_o;  // block-table entries for even / odd rounds
+    if (n_u > 0) {
       int p0a, p0b;
-      stage_pids(st0, p0a, p0b);
-      stage_pids(st0 + 1, pa_o, pb_o);
-      stage_load(ra, p0a, p0b, true);
-      stage_pids(st0 + 2, pa_e, pb_e);
-      stage_load(rb, pa_o, pb_o, 1 < n_stages);
-      stage_store(ra, st0, 0);
+      stage_pids(stage_of(0), p0a, p0b);
+      stage_pids(stage_of(1), pa_o, pb_o);
+      stage_load(ra, p0a, p0b, live_of(0));
+      stage_pids(stage_of(2), pa_e, pb_e);
+      stage_load(rb, pa_o, pb_o, live_of(1));
+      stage_store(ra, stage_of(0), 0);
     }
     // An explicit use of q here, after the prologue has waited for younger loads: the
     // compiler's wait counts then know q has arrived on every path into the loop, instead
     // of waiting for it (and every load issued after it) at the top of each trip.
     asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
     __syncthreads();
-    // One iteration for stage st of parity P (0: st even).  Registers are chosen by name at
-    // compile time (stage u lives in ra for even u, rb for odd u; the block-table entries of
-    // stage u in pa_e/pb_e or pa_o/pb_o by the parity of u) so nothing is addressed through
-    // a pointer and no register set spills to scratch.
-    auto iteration = [&](int st, auto parity) __attribute__((always_inline)) {
+    auto iteration = [&](int u, auto parity) __attribute__((always_inline)) {
       constexpr int P = decltype(parity)::value;
-      const int buf = st & 1;
-      // block-table entries of stage st + 3 (parity !P) ; K/V of stage st + 2 (parity P)
+      const int buf = u & 1;
       if constexpr (P == 0) {
-        stage_pids(st0 + st + 3, pa_o, pb_o);
-        stage_load(ra, pa_e, pb_e, st + 2 < n_stages);
+        stage_pids(stage_of(u + 3), pa_o, pb_o);
+        stage_load(ra, pa_e, pb_e, live_of(u + 2));
       } else {
-        stage_pids(st0 + st + 3, pa_e, pb_e);
-        stage_load(rb, pa_o, pb_o, st + 2 < n_stages);
+        stage_pids(stage_of(u + 3), pa_e, pb_e);
+        stage_load(rb, pa_o, pb_o, live_of(u + 2));
       }
-      compute_stage_fast(buf, (st0 + st) * kStage);
-      // Stored on every iteration, also past the last stage (the other buffer is not read
-      // again then): a store skipped on some paths would leave its loads pending at the loop
-      // back edge, and the compiler then waits for every load at the top of the loop.
+      if (live_of(u)) compute_stage_fast(buf, stage_of(u) * kStage);
+      // Stored on every round, also past the last one (the other buffer is not read
+      // again then): a store skipped on some paths would leave its loads pending at the
+      // loop back edge, and the compiler then waits for every load at the top of the loop.
       if constexpr (P == 0)
-        stage_store(rb, st0 + st + 1, buf ^ 1);
+        stage_store(rb, stage_of(u + 1), buf ^ 1);
       else
-        stage_store(ra, st0 + st + 1, buf ^ 1);
+        stage_store(ra, stage_of(u + 1), buf ^ 1);
       __syncthreads();
     };
-    // Pairs of stages, then an odd last stage alone: the loop has a single back edge and
-    // one exit, so the compiler's wait at the loop top covers only the block-table entries,
-    // not the K/V loads meant to stay in flight (an exit between the two halves made it
-    // wait for every load there).  The odd last stage has nothing left to load or store.
-    int st = 0;
-    for (; st + 1 < n_stages; st += 2) {
-      iteration(st, std::integral_constant<int, 0>{});
-      iteration(st + 1, std::integral_constant<int, 1>{});
+    int u = 0;
+    for (; u + 1 < n_u; u += 2) {
+      iteration(u, std::integral_constant<int, 0>{});
+      iteration(u + 1, std::integral_constant<int, 1>{});
     }
-    if (st < n_stages) compute_stage_fast(st & 1, (st0 + st) * kStage);
+    if (u < n_u && live_of(u)) compute_stage_fast(u & 1, stage_of(u) * kStage);
+  }
+
+  if constexpr (G > 1) {
+    // Merge of the key groups through LDS (the stage buffers are free once every group
+    // has finished): groups 1 .. G-1 leave their reference maxima, lane sums and output
+    // accumulators; group 0 combines them, M = max m_g, weights 2^(m_g - M) (0 for a
+    // group that saw no key of the row), and goes on with the result alone.
+    constexpr int kF = 34;  // floats per lane: o0, o1, m, lsum
+    float* mb = reinterpret_cast<float*>(sh_all);
+    __syncthreads();
+    if (grp > 0) {
+      float* dst = mb + ((size_t)((grp - 1) * kGroup + w) * kF) * 64 + lane;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dst[r * 64] = o0[r];
+        dst[(16 + r) * 64] = o1[r];
+      }
+      dst[32 * 64] = m;
+      dst[33 * 64] = lsum;
+    }
+    __syncthreads();
+    if (grp > 0) return;
+    float mg[G - 1], M = m;
+#pragma unroll
+    for (int k = 1; k < G; ++k) {
+      mg[k - 1] = mb[((size_t)((k - 1) * kGroup + w) * kF + 32) * 64 + lane];
+      M = vmax(M, mg[k - 1]);
+    }
+    const float f0 = m == kNegInf ? 0.f : fast_exp2(m - M);
+    lsum *= f0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o0[r] *= f0;
+      o1[r] *= f0;
+    }
+#pragma unroll
+    for (int k = 1; k < G; ++k) {
+      const float* srcp = mb + ((size_t)((k - 1) * kGroup + w) * kF) * 64 + lane;
+      const float f = mg[k - 1] == kNegInf ? 0.f : fast_exp2(mg[k - 1] - M);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o0[r] = __builtin_fmaf(f, srcp[r * 64], o0[r]);
+        o1[r] = __builtin_fmaf(f, srcp[(16 + r) * 64], o1[r]);
+      }
+      lsum = __builtin_fmaf(f, srcp[33 * 64], lsum);
+    }
+    m = M;
   }
 
   if (n_split > 1) {
@@ -581,10 +627,17 @@ PrefillPlan plan_prefill(int n_seqs, int max_q_len, int max_ctx_len, int num_kv_
   PrefillPlan p{};
   const int64_t items = (int64_t)((max_q_len + kQTile - 1) / kQTile) * n_seqs * num_kv_heads;
   const int64_t stages = std::max<int64_t>(1, ((int64_t)max_ctx_len + kStage - 1) / kStage);
+  const int64_t cus = std::max(compute_units, 1);
   p.items = items;
+  // A grid smaller than the chip gives each tile two key groups (eight waves), halving the
+  // serial stage chain of its workgroup; a larger one keeps three four-wave workgroups
+  // per compute unit.
+  p.groups = items > 0 && items < cus ? 2 : 1;
   int64_t split = kv_splits;
-  if (split == 0) {  // enough workgroups for two per compute unit, at most 8 pieces
-    const int64_t want = 2 * (int64_t)std::max(compute_units, 1);
+  if (split == 0) {  // at most 8 pieces, never more than the stages
+    // one-group workgroups: enough for two per compute unit; two-group ones: enough for
+    // half the compute units (the pieces' merge costs more than the idle units)
+    const int64_t want = p.groups == 2 ? cus / 2 : 2 * cus;
     split = items > 0 && items < want ? (want + items - 1) / items : 1;
     split = std::min<int64_t>(std::min<int64_t>(split, kPrefillMaxSplit), stages);
   }
@@ -602,7 +655,7 @@ hipError_t launch_prefill(const LaunchGeom& geo, const PrefillPlan& plan, void* 
   const int n_qtiles = (max_q_len + kQTile - 1) / kQTile;
   const int ns = plan.split;
   const dim3 grid((unsigned)(plan.items * ns));
-  const dim3 block(kThreads);
+  const dim3 block(kThreads * plan.groups);
   const float qk_scale = scale * kLog2e;
   auto* o = static_cast<uint16_t*>(out);
   auto* qq = static_cast<const uint16_t*>(q);
@@ -614,15 +667,16 @@ hipError_t launch_prefill(const LaunchGeom& geo, const PrefillPlan& plan, void* 
     ws_o = static_cast<float*>(workspace);
     ws_ml = reinterpret_cast<float2*>(ws_o + (size_t)plan.items * ns * kSlotFloats);
   }
+#define PA_PREFILL_LAUNCH(B, NG)                                                              \
+  hipLaunchKernelGGL((prefill_kernel<B, NG>), grid, block, 0, stream, o, qq, kp, vp, block_tables, \
+                     max_blocks, cu_q_lens, ctx_lens, n_seqs, n_qtiles, geo.num_pages,            \
+                     geo.num_kv_heads, qk_scale, causal, ns, ws_o, ws_ml)
   if (geo.block_size == 16) {
-    hipLaunchKernelGGL(prefill_kernel<16>, grid, block, 0, stream, o, qq, kp, vp, block_tables,
-                       max_blocks, cu_q_lens, ctx_lens, n_seqs, n_qtiles, geo.num_pages,
-                       geo.num_kv_heads, qk_scale, causal, ns, ws_o, ws_ml);
+    if (plan.groups == 2) PA_PREFILL_LAUNCH(16, 2); else PA_PREFILL_LAUNCH(16, 1);
   } else {
-    hipLaunchKernelGGL(prefill_kernel<32>, grid, block, 0, stream, o, qq, kp, vp, block_tables,
-                       max_blocks, cu_q_lens, ctx_lens, n_seqs, n_qtiles, geo.num_pages,
-                       geo.num_kv_heads, qk_scale, causal, ns, ws_o, ws_ml);
+    if (plan.groups == 2) PA_PREFILL_LAUNCH(32, 2); else PA_PREFILL_LAUNCH(32, 1);
   }
+#undef PA_PREFILL_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   const dim3 mgrid((unsigned)(plan.items * kGroup));

@@ -235,7 +235,7 @@ def _prefill_ws(n_seqs, max_q, max_ctx, hkv, splits, cus=256):
     stages = max(1, -(-max_ctx // 64))
     p = splits
     if p == 0:
-        want = 2 * cus
+        want = cus // 2 if 0 < items < cus else 2 * cus  # two key groups below cus tiles
         p = -(-want // items) if 0 < items < want else 1
         p = min(p, 8, stages)
     p = max(p, 1)
@@ -246,7 +246,8 @@ def test_prefill_workspace_bytes(lib):
     g = geom()
     for n, mq, mc, sp in ((8, 1024, 1024, 0), (1, 512, 1024, 0), (2, 32, 64, 0), (1, 1, 1, 0),
                           (3, 100, 300, 3), (5, 40, 40, 1), (0, 32, 64, 0), (4, 0, 64, 0),
-                          (1, 64, 4096, 0), (64, 2048, 2048, 0)):
+                          (1, 64, 4096, 0), (64, 2048, 2048, 0), (1, 512, 512, 0),
+                          (4, 128, 1024, 0), (2, 64, 64, 0)):
         assert lib.pa_prefill_workspace_bytes(g, n, mq, mc, sp) == _prefill_ws(n, mq, mc, 8, sp)
     assert lib.pa_prefill_workspace_bytes(g, 2, 32, 64, -1) == 0  # invalid: nothing to size
 

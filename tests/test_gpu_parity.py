@@ -274,6 +274,21 @@ def test_prefill_key_splits(splits, causal):
     assert_close(out, ref, f"prefill kv_splits={splits} causal={causal}")
 
 
+@pytest.mark.parametrize("splits", [1, 2, 5, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_key_groups_and_splits_small_grid(splits, causal):
+    # fewer tiles than compute units: two key groups per workgroup, merged in LDS, and on
+    # top of that the pieces (a piece of one or two stages leaves the second group idle)
+    case = W.custom_case([70, 33, 129, 1, 640], [7, 33, 100, 1, 96], kind="prefill",
+                         block_size=32, seed=92)
+    _announce(f"prefill small grid kv_splits={splits} causal={causal}")
+    g = GpuCase(case)
+    out = g.prefill(causal=causal, kv_splits=splits)
+    kp, vp = oracle_pools(case)
+    ref = oracle_prefill(case, kp, vp, causal=causal)
+    assert_close(out, ref, f"small grid kv_splits={splits} causal={causal}")
+
+
 @pytest.mark.parametrize("splits", [1, 4])
 def test_prefill_out_of_range_page_gives_nan_rows(splits):
     # a block-table entry outside the pool: exactly the rows whose keys reach that block
