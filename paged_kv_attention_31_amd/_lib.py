@@ -6,7 +6,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+# PAGEDATTN_LIB names another build of the same library (the host-sanitized test build).
+LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARG = -1
