@@ -253,10 +253,9 @@ int pa_rope_kv_append(pa_geom_t g, const void* q, void* q_out, const void* k_new
  *                   56 * num_kv_heads tiles.  Other values give PA_ERR_INVALID_ARG.
  *   workspace       device scratch of at least pa_decode_workspace_bytes(...) bytes
  *                   for the same arguments (on the same device); may be NULL when that
- *                   size is 0.  With W workers and S = n_seqs * num_kv_heads + W it is
- *                   S * 4 * (64 * 4 + 8) + 8 * (W + 1) bytes (fp32 partials, then W + 1
- *                   int32 pairs), or 0 when no pair can be split (ceil(max_ctx_len/64) <= 1
- *                   or W = 1).  Its contents need no initialisation and are scratch
+ *                   size is 0.  With W workers it is 2W * 4 * (64 * 4 + 8) + 8 * (W + 1)
+ *                   bytes (two fp32 partial slots per worker, then W + 1 int32 pairs), or
+ *                   0 when no pair can be split (ceil(max_ctx_len/64) <= 1 or W = 1).  Its contents need no initialisation and are scratch
  *                   after the call; concurrent calls need separate workspaces.
  * pa_decode_partition_tokens returns the most tokens one worker streams for these
  * arguments (a multiple of 64), or a negative status.
@@ -300,9 +299,10 @@ int pa_decode_append(pa_geom_t g, void* out, const void* q, const void* k_new,
  * go to a device array of the library's own, PA_DECODE_SCRATCH_BYTES per device, held
  * until the process ends.  The call allocates and frees nothing.  It returns
  * PA_ERR_WORKSPACE, before any launch, when pa_decode_workspace_bytes(...) for the same
- * arguments exceeds PA_DECODE_SCRATCH_BYTES (with the automatic partition on MI355X that
- * is about n_seqs * num_kv_heads + 1024 > 15800, e.g. more than 1900 sequences at 8 KV
- * heads once any context exceeds 64 tokens).  The scratch needs no initialisation.  Every
+ * arguments exceeds PA_DECODE_SCRATCH_BYTES, i.e. with more than 7935 workers (the
+ * automatic partition uses four per compute unit, 1024 on MI355X, unless a batch needs
+ * more; a small explicit partition_tokens can ask for more).  The scratch needs no
+ * initialisation.  Every
  * call on one device shares that device's array: calls that overlap in time on one
  * device (other streams, other threads) race on it and must be serialised by the caller.
  * ------------------------------------------------------------------------------- */

@@ -141,6 +141,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   auto ctx_code = [&](int raw) { return min(max(raw, 0), APPEND ? ctx_cap + 1 : ctx_cap); };
 
   __shared__ int scan_sh[257];
+  // the context-length codes of the first kDecodeCtxCache sequences, read once for the
+  // prefix sum and reused to locate the wave's first segment (no second global round trip)
+  __shared__ int ctx_sh[kDecodeCtxCache];
+  const bool ctx_cached = n_seqs <= kDecodeCtxCache;
   __shared__ int wsum_sh[kDecodeWaves];
   __shared__ uint4 q_sh[kDecodeWaves][2][kGroup][8];  // [wave][slot][head][piece]
   // probabilities of the tile as two bf16 terms, p = hi + lo: [wave][term][head][token]
@@ -154,7 +158,11 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   int mine = 0;
   for (int j = 0; j < chunk; ++j) {
     const int s = tid * chunk + j;
-    if (s < n_seqs) mine += tiles_of(min(ctx_code(ctx_lens[s]), ctx_cap));
+    if (s < n_seqs) {
+      const int code = ctx_code(ctx_lens[s]);
+      if (ctx_cached) ctx_sh[s] = code;
+      mine += tiles_of(min(code, ctx_cap));
+    }
   }
   int incl = mine;
 #pragma unroll
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   int64_t cum = uni(scan_sh[lo]);
   for (int s0 = lo * chunk; s0 < n_seqs; s0 += 64) {
     const int sj = s0 + lane;
-    const int cj = sj < n_seqs ? ctx_code(ctx_lens[sj]) : 0;
+    const int cj = sj < n_seqs ? (ctx_cached ? ctx_sh[sj] : ctx_code(ctx_lens[sj])) : 0;
     const int nj = sj < n_seqs ? tiles_of(min(cj, ctx_cap)) : 0;
     int pre = nj;
 #pragma unroll
@@ -227,7 +235,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   // tiles long (the host sizes the worker count for that) and every sequence holds at
   // least Hkv tiles, so a range touches at most 58 sequences.
   const int cache_base = cc.s;
-  const int cache_ctx = cache_base + lane < n_seqs ? ctx_code(ctx_lens[cache_base + lane]) : 0;
+  const int cache_ctx =
+      cache_base + lane < n_seqs
+          ? (ctx_cached ? ctx_sh[cache_base + lane] : ctx_code(ctx_lens[cache_base + lane]))
+          : 0;
   auto advance = [&](Cursor& c) {
     if (++c.i == c.nt) {
       c.i = 0;
@@ -467,7 +478,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   };
 
   // End of a segment's part in this range: the bf16 output if the whole segment was
-  // here, else an fp32 partial in slot (s * Hkv + g) + wid.  The wave that holds the
+  // here, else an fp32 partial.  A range cuts at most two segments, its first (cut at its
+  // start) and its last (cut at its end), so wave wid has two partial slots: 2 wid for
+  // its first segment, 2 wid + 1 for a last segment whose first tile it holds.  The wave that holds the
   // first tile of a cut segment (its last segment) records (segment, number of covering
   // waves) for the merge; wave(t) = floor(((t + 1) * n_eff - 1) / n_tiles) is the range
   // holding stream tile t.
@@ -537,7 +550,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       // the owner records the stream index of the segment's last tile; the merge finds
       // the wave holding it
       if (started) own = make_int2(seg, (int)(c.first + (int64_t)c.g * c.nt + c.nt - 1));
-      const size_t slot = (size_t)seg + wid;
+      const size_t slot = 2 * (size_t)wid + (started ? 1 : 0);
       acc[0][0] = f[0];
       acc[0][1] = f[1];
       acc[0][2] = f[2];
@@ -628,14 +641,16 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 // descriptor names the segment it owns (it holds the segment's first tile) and the
 // stream index of the segment's last tile; with the header (stream length T, waves E)
 // the wave holding that tile is w1 = floor(((last + 1) E - 1) / T), so np = w1 - wid + 1
-// consecutive waves left partials for the segment, in slots seg + wid .. seg + w1:
-// M = max_j m_j, L = sum_j l_j 2^(m_j - M), out = sum_j o_j 2^(m_j - M) / L, the sums
-// taken in ascending wave order.  Lane = head dimension; the (m, l) pairs and the
-// outputs are loaded lane-parallel.
+// consecutive waves left partials for the segment: the owner in its slot 2 wid + 1, each
+// later wave w in its slot 2 w.  M = max_j m_j, L = sum_j l_j 2^(m_j - M),
+// out = sum_j o_j 2^(m_j - M) / L, the sums taken in ascending wave order.  Lane = head
+// dimension.  The first two partials are loaded together with the descriptor (nearly every
+// wave owns a cut segment, and a cut segment has at least two), so a merge needs one
+// memory round trip; further partials follow four per round.
 // With k_new set (pa_decode_append), each wave first writes the new K/V rows of the
 // (sequence, KV head) pairs seg = wid, wid + n_workers, ... into their pool slots (position
-// ctx_lens[s] - 1; nothing for an empty context or an out-of-range page id): lanes 0..7
-// store the K row's 16-byte pieces, lane d the V element of dimension d.
+// ctx_lens[s] - 1; nothing for an empty context, an out-of-range page id or a length past
+// the cap): lanes 0..7 store the K row's 16-byte pieces, lane d the V element of dimension d.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
     const int2* __restrict__ ws_desc, int n_workers, int num_kv_heads,
@@ -666,29 +681,42 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     }
   }
   if (wid >= n_workers || ws_desc == nullptr) return;
+  // partial j of the segment wid owns: slot 2 wid + 1 for j = 0, 2 (wid + j) after
+  const int n_slots = 2 * n_workers;
+  auto slot_of = [&](int j) { return min(j == 0 ? 2 * wid + 1 : 2 * (wid + j), n_slots - 1); };
+  // the first two partials, issued with the descriptor
+  float2 mlv[4][kGroup];
+  float ov[4][kGroup];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const size_t sl = (size_t)slot_of(u);
+#pragma unroll
+    for (int h = 0; h < kGroup; ++h) {
+      mlv[u][h] = ws_ml[sl * kGroup + h];
+      ov[u][h] = ws_o[(sl * kGroup + h) * kHeadDim + lane];
+    }
+  }
   const int2 desc = ws_desc[wid];
+  const int2 hdr = ws_desc[n_workers];  // (tiles in the stream, workers)
   const int seg = desc.x;
   if (seg < 0) return;
-  const int2 hdr = ws_desc[n_workers];  // (tiles in the stream, workers)
   const int w_last = (int)((((int64_t)desc.y + 1) * hdr.y - 1) / hdr.x);  // holds tile desc.y
   const int np = w_last - wid + 1;
   if (np < 2) return;
   const int s = seg / num_kv_heads;
   const int g = seg - s * num_kv_heads;
   const int hq = num_kv_heads * kGroup;
-  const float2* ml = ws_ml + ((size_t)seg + wid) * kGroup;          // [np][4]
-  const float* o = ws_o + ((size_t)seg + wid) * kGroup * kHeadDim;  // [np][4][64]
   float M[kGroup], L[kGroup], O[kGroup];
 #pragma unroll
   for (int h = 0; h < kGroup; ++h) {
-    M[h] = kNegInf;
+    M[h] = fmaxf(mlv[0][h].x, mlv[1][h].x);
     L[h] = 0.f;
     O[h] = 0.f;
   }
-  // maxima, 16 partials (64 (m, l) pairs) per load round
-  for (int b = 0; b < np; b += 16) {
-    const int j = b * kGroup + lane;
-    const float mj = j < np * kGroup ? ml[j].x : kNegInf;
+  // maxima of the partials past the first two, 16 partials (64 (m, l) pairs) per round
+  for (int b = 2; b < np; b += 16) {
+    const int j = b + (lane >> 2);
+    const float mj = j < np ? ws_ml[(size_t)slot_of(j) * kGroup + (lane & 3)].x : kNegInf;
     float x0 = (lane & 3) == 0 ? mj : kNegInf;
     float x1 = (lane & 3) == 1 ? mj : kNegInf;
     float x2 = (lane & 3) == 2 ? mj : kNegInf;
@@ -699,24 +727,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     M[2] = fmaxf(M[2], x2);
     M[3] = fmaxf(M[3], x3);
   }
-  // weights and sums in ascending partial order, four partials per load round
-  for (int v = 0; v < np; v += 4) {
-    float2 mlv[4][kGroup];
-    float ov[4][kGroup];
+  // weights and sums in ascending partial order: the first two from registers, the rest
+  // four per load round
+  auto accumulate = [&](int count) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int h = 0; h < kGroup; ++h) {
-        const bool live = v + u < np;
-        mlv[u][h] = live ? ml[(v + u) * kGroup + h] : make_float2(kNegInf, 0.f);
-        ov[u][h] = live ? o[((size_t)(v + u) * kGroup + h) * kHeadDim + lane] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int h = 0; h < kGroup; ++h) {
-        if (v + u < np) {
+        if (u < count) {
           const float f = M[h] == kNegInf || mlv[u][h].x == kNegInf
                               ? 0.f
                               : fast_exp2(mlv[u][h].x - M[h]);
@@ -725,6 +743,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
         }
       }
     }
+  };
+  accumulate(2);
+  for (int v = 2; v < np; v += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool live = v + u < np;
+      const size_t sl = (size_t)slot_of(live ? v + u : 0);
+#pragma unroll
+      for (int h = 0; h < kGroup; ++h) {
+        mlv[u][h] = live ? ws_ml[sl * kGroup + h] : make_float2(kNegInf, 0.f);
+        ov[u][h] = live ? ws_o[(sl * kGroup + h) * kHeadDim + lane] : 0.f;
+      }
+    }
+    accumulate(min(4, np - v));
   }
 #pragma unroll
   for (int h = 0; h < kGroup; ++h)
@@ -750,7 +782,7 @@ DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partit
   p.tiles_per_worker = (n_max + workers - 1) / workers;
   p.merge = workers > 1 && tiles_per_seq > 1;
   if (p.merge) {
-    const int64_t slots = (int64_t)n_seqs * num_kv_heads + workers;
+    const int64_t slots = 2 * workers;  // two partial slots per worker
     p.ws_bytes = (size_t)slots * kGroup * (kHeadDim * sizeof(float) + sizeof(float2)) +
                  (size_t)(workers + 1) * sizeof(int2);
   }
@@ -767,7 +799,7 @@ hipError_t launch_decode(const LaunchGeom& geo, const DecodePlan& plan, void* ou
   float2* ws_ml = nullptr;
   int2* ws_desc = nullptr;
   if (plan.merge) {
-    const size_t slots = (size_t)n_seqs * geo.num_kv_heads + plan.workers;
+    const size_t slots = 2 * (size_t)plan.workers;
     ws_o = static_cast<float*>(workspace);
     ws_ml = reinterpret_cast<float2*>(ws_o + slots * kGroup * kHeadDim);
     ws_desc = reinterpret_cast<int2*>(ws_ml + slots * kGroup);

@@ -55,6 +55,8 @@ constexpr int kDecodeWaves = 4;
 // A worker's range is at most this many tiles per KV head (so it touches at most this
 // many sequences plus two, which its lanes can hold).
 constexpr int kDecodeMaxSeqsPerRange = 56;
+// Sequences whose context lengths a decode workgroup keeps in LDS (beyond, it re-reads them).
+constexpr int kDecodeCtxCache = 4096;
 
 // How a decode call is cut into workers; identical on the sizing and the launch side.
 struct DecodePlan {

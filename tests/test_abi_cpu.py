@@ -184,13 +184,18 @@ def test_decode_noalloc_validation_and_scratch_limit(lib):
     assert _decode_noalloc(lib, scale=float("nan")) == _lib.PA_ERR_INVALID_ARG
     assert _decode_noalloc(lib, n=0, out=None) == 0
     assert _lib.PA_DECODE_SCRATCH_BYTES == 16 << 20
-    # the largest batch that fits, and the first that does not (contexts of 2 tiles)
+    # the partials take two slots per worker whatever the batch: the automatic partition
+    # (1024 workers here) always fits, and a partition of one tile per worker fits up to
+    # 7935 workers (contexts of 2 tiles: n_seqs * 8 * 2 workers)
     g = geom(num_pages=4096)
-    fits = [n for n in range(1000, 3000, 10)
-            if _plan_ws(n, 128, 8, 0) <= _lib.PA_DECODE_SCRATCH_BYTES]
-    n_big = max(fits) + 10
-    assert lib.pa_decode_workspace_bytes(g, n_big, 128, 0) > _lib.PA_DECODE_SCRATCH_BYTES
-    assert _decode_noalloc(lib, g=g, n=n_big, max_blocks=8, max_ctx=128) == _lib.PA_ERR_WORKSPACE
+    assert lib.pa_decode_workspace_bytes(g, 20000, 128, 0) == _plan_ws(20000, 128, 8, 0)
+    assert _plan_ws(20000, 128, 8, 0) <= _lib.PA_DECODE_SCRATCH_BYTES
+    fits = [n for n in range(400, 600) if _plan_ws(n, 128, 8, 64) <= _lib.PA_DECODE_SCRATCH_BYTES]
+    n_big = max(fits) + 1
+    assert lib.pa_decode_workspace_bytes(g, max(fits), 128, 64) <= _lib.PA_DECODE_SCRATCH_BYTES
+    assert lib.pa_decode_workspace_bytes(g, n_big, 128, 64) > _lib.PA_DECODE_SCRATCH_BYTES
+    assert _decode_noalloc(lib, g=g, n=n_big, max_blocks=8, max_ctx=128,
+                           part=64) == _lib.PA_ERR_WORKSPACE
 
 
 def _plan_ws(n_seqs, max_ctx, hkv, part, cus=256):
@@ -202,7 +207,7 @@ def _plan_ws(n_seqs, max_ctx, hkv, part, cus=256):
     workers = max(1, min(workers, n_max))
     if workers == 1 or tiles == 1:
         return 0
-    return (n_seqs * hkv + workers) * 4 * (64 * 4 + 8) + 8 * (workers + 1)
+    return 2 * workers * 4 * (64 * 4 + 8) + 8 * (workers + 1)
 
 
 def test_partition_choice(lib):
