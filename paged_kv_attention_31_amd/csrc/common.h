@@ -116,6 +116,21 @@ __device__ __forceinline__ void wave_max4(float& a, float& b, float& c, float& d
   d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, d), 63));
 }
 
+// Inclusive prefix sum over the 64 lanes, in every lane: a Hillis-Steele scan inside each
+// row of 16 lanes (DPP row shifts by 1, 2, 4 and 8; a lane with no source adds 0), then
+// the totals of the rows below, read back per row.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
+}
+
 __device__ __forceinline__ float shfl_xor_f(float x, int m) {
   return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, x), m, kWave));
 }

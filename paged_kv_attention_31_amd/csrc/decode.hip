@@ -164,12 +164,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       mine += tiles_of(min(code, ctx_cap));
     }
   }
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += y;
-  }
+  const int incl = wave_incl_scan(mine, lane);
   if (lane == 63) wsum_sh[w] = incl;
   __syncthreads();
   int before = 0;
@@ -193,24 +188,28 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   const int64_t a = (int64_t)wid * n_tiles / n_eff;
   const int L = (int)((int64_t)(wid + 1) * n_tiles / n_eff - a);
 
-  // chunk holding tile a, then the sequence inside it (64 sequences per step)
-  int lo = 0, hi = 255;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)uni(scan_sh[mid]) * hkv <= a) lo = mid; else hi = mid - 1;
-  }
+  // Chunk holding tile a: the chunk prefix is non-decreasing, so it is the number of chunk
+  // starts at or below a, less one (lane l checks chunks 4 l .. 4 l + 3 at once).
+  int n_le = 0;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj)
+    n_le += __popcll(__ballot((int64_t)scan_sh[4 * lane + jj] * hkv <= a));
+  const int lo = uni(n_le) - 1;
   Cursor cc{-1, 0, 0, 0, 1, 0, false};
   int64_t cum = uni(scan_sh[lo]);
-  for (int s0 = lo * chunk; s0 < n_seqs; s0 += 64) {
+  if (chunk == 1) {  // a chunk is one sequence: tile a lies in sequence lo
+    const int code = uni(ctx_sh[lo]);
+    cc.s = lo;
+    cc.ctx = min(code, ctx_cap);
+    cc.over = code > ctx_cap;
+    cc.nt = tiles_of(cc.ctx);
+  }
+  // else the sequence inside the chunk, 64 sequences per step
+  for (int s0 = lo * chunk; cc.s < 0 && s0 < n_seqs; s0 += 64) {
     const int sj = s0 + lane;
     const int cj = sj < n_seqs ? (ctx_cached ? ctx_sh[sj] : ctx_code(ctx_lens[sj])) : 0;
     const int nj = sj < n_seqs ? tiles_of(min(cj, ctx_cap)) : 0;
-    int pre = nj;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(pre, off, kWave);
-      if (lane >= off) pre += y;
-    }
+    const int pre = wave_incl_scan(nj, lane);
     const uint64_t hit = __ballot(a < (int64_t)hkv * (cum + pre));
     if (hit) {
       const int j = __ffsll((unsigned long long)hit) - 1;
