@@ -15,8 +15,12 @@ Prints one JSON line.  ``value`` = decode KV bytes read per step / wall time per
 (whole step, all kernels), the step captured once in a HIP graph and replayed (the eager
 step time is reported beside it).  ``roofline`` reports the dominant kernel (pa_decode, timed
 with HIP events on its stream) against HBM peak; ``roofline_prefill`` reports pa_prefill
-against dense bf16 MFMA peak.  ``cpu_baseline`` times the CPU oracle on a bounded sample
-of the same workload (layer 0) before the GPU is touched.
+against dense bf16 MFMA peak.  The same default run then measures the other targets'
+own workloads and adds them to the line: ``roofline_prefill_8prompts`` (pa_prefill on the
+8-prompt workload), ``roofline_decode_batched`` and ``roofline_decode_long`` (the
+64-sequence and 16 x 32k decode steps, one pa_decode_append launch per layer, with pa_decode
+beside it).  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload
+(layer 0) on a process pool over the host's cores, before the GPU is touched.
 
 ``--workload rope-append`` times pa_rope_kv_append alone (RoPE of Q and K fused with the
 K/V append) on the 4622 new rows of the prefill workload, against HBM peak, with the
@@ -324,6 +328,37 @@ class HeadStart:
             self.torch.cuda._sleep(self.cycles)
 
 
+def decode_rooflines(res: dict, base: W.Case, traffic_key: str):
+    """The line's decode entries: pa_decode against HBM peak, or, when the step ran as one
+    pa_decode_append launch per layer, that launch as `roofline` with pa_decode beside it
+    as `roofline_decode_only`.  Returns (entries, step_timing additions)."""
+    ach = res["decode_gbps"]
+    dec_line = {"bound": "hbm",
+                "kernel": "pa_decode (decode_stream_kernel + decode_merge_kernel)",
+                "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4),
+                "traffic": hbm_traffic(traffic_key),
+                "bytes_per_launch": res["decode_bytes_per_launch"],
+                "unique_bytes_per_launch": unique_kv_bytes(base),
+                "avg_launch_ms": round(res["decode_ms"], 5)}
+    fz = res.get("fused")
+    if fz is None:
+        return {"roofline": dec_line}, {}
+    # the step that value times: one pa_decode_append launch per layer
+    extra = {"fused_append": True, "separate_append_graph_ms": round(fz["separate_ms_per_step"], 4),
+             "separate_append_value": round(fz["separate_value"], 2)}
+    ach = fz["kernel_gbps"]
+    fused = {"bound": "hbm",
+             "kernel": "pa_decode_append (decode_stream_kernel<bs, append> + decode_merge_kernel)",
+             "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": hbm_traffic(traffic_key),
+             "bytes_per_launch": res["decode_bytes_per_launch"],
+             "unique_bytes_per_launch": unique_kv_bytes(base),
+             "avg_launch_ms": round(fz["kernel_ms"], 5)}
+    dec_line["traffic"] = None  # the counters are taken on the fused launch
+    return {"roofline": fused, "roofline_decode_only": dec_line}, extra
+
+
 def prefill_roofline(res: dict, base: W.Case, traffic_key: str) -> dict:
     """pa_prefill against dense bf16 MFMA peak, and the least HBM traffic the launch needs
     (q and out once, each sequence's K/V once) at the measured time against HBM peak: the
@@ -420,7 +455,10 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     # enqueueing, so the launches run back to back and the events time the GPU alone.
     # Events around single launches are not used: on this runtime they can read several
     # times the kernel's duration when the host falls behind.
-    hold = HeadStart(torch, stream, host_s)
+    # A batch holds at least 16 launches (the layer loop repeated for workloads of few
+    # layers) so the first launch's start-up is spread over many.
+    reps = max(1, -(-16 // n_layers))
+    hold = HeadStart(torch, stream, host_s * reps)
     kinds = [("append", launch_append)] + ([("prefill", launch_prefill)] if n_pre else []) + \
         ([("decode", launch_decode)] if n_dec else [])
     ev = {k: [] for k, _ in kinds}
@@ -430,8 +468,9 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
         for k, fn in kinds:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            for L in layers:
-                fn(L, stream)
+            for _r in range(reps):
+                for L in layers:
+                    fn(L, stream)
             b.record(stream)
             ev[k].append((a, b))
     torch.cuda.synchronize()
@@ -453,8 +492,8 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    def avg_ms(pairs):  # per launch: each pair brackets one launch per layer
-        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) / n_layers if pairs else 0.0
+    def avg_ms(pairs):  # per launch: each pair brackets reps launches per layer
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs])) / (n_layers * reps) if pairs else 0.0
 
     # A pure decode step (one new token per sequence, no prefill) also runs as one
     # pa_decode_append launch per layer: timed per launch (events) and as a graph, and
@@ -474,11 +513,12 @@ def run_gpu(cfg: int, steps: int, warmup: int, partition: int = 0) -> dict:
         for _ in range(warmup):
             fused_step(stream)
         torch.cuda.synchronize()
-        for _ in range(steps):  # a batch of one launch per layer, as above
+        for _ in range(steps):  # a batch of reps launches per layer, as above
             hold()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            fused_step(stream)
+            for _r in range(reps):
+                fused_step(stream)
             b.record(stream)
             ev_fused.append((a, b))
         torch.cuda.synchronize()
@@ -652,6 +692,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill-target", action="store_true",
                     help="mixed workload: skip the 8-prompt prefill measurement")
+    ap.add_argument("--no-decode-targets", action="store_true",
+                    help="mixed workload: skip the batched and long-context decode measurements")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--partition", type=int, default=0,
                     help="decode KV tokens per split-K partition (0 = the library's choice)")
@@ -710,34 +752,9 @@ def main() -> int:
                         "eager_ms": round(res["ms_per_step_eager"], 4)},
     }
     if "decode_ms" in res:
-        ach = res["decode_gbps"]
-        dec_line = {"bound": "hbm",
-                    "kernel": "pa_decode (decode_stream_kernel + decode_merge_kernel)",
-                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBPS, 4),
-                    "traffic": hbm_traffic(args.workload),
-                    "bytes_per_launch": res["decode_bytes_per_launch"],
-                    "unique_bytes_per_launch": unique_kv_bytes(base),
-                    "avg_launch_ms": round(res["decode_ms"], 5)}
-        fz = res.get("fused")
-        if fz is not None:
-            # the step that value times: one pa_decode_append launch per layer
-            line["step_timing"].update(
-                fused_append=True, separate_append_graph_ms=round(fz["separate_ms_per_step"], 4),
-                separate_append_value=round(fz["separate_value"], 2))
-            ach = fz["kernel_gbps"]
-            line["roofline"] = {
-                "bound": "hbm",
-                "kernel": "pa_decode_append (decode_stream_kernel<bs, append> + decode_merge_kernel)",
-                "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": hbm_traffic(args.workload),
-                "bytes_per_launch": res["decode_bytes_per_launch"],
-                "unique_bytes_per_launch": unique_kv_bytes(base),
-                "avg_launch_ms": round(fz["kernel_ms"], 5)}
-            dec_line["traffic"] = None  # the counters are taken on the fused launch
-            line["roofline_decode_only"] = dec_line
-        else:
-            line["roofline"] = dec_line
+        rl, extra = decode_rooflines(res, base, args.workload)
+        line.update(rl)
+        line["step_timing"].update(extra)
     if "prefill_ms" in res:
         key = "roofline_prefill" if "roofline" in line else "roofline"
         line[key] = prefill_roofline(res, base, args.workload + "-prefill"
@@ -750,6 +767,19 @@ def main() -> int:
         line["roofline_prefill_8prompts"] = dict(
             {"workload": W.CONFIG_NAMES[3], "layer_copies": res3["n_layers"]},
             **prefill_roofline(res3, base3, "prefill"))
+    if args.workload == "mixed" and not args.no_decode_targets:
+        # the pure decode workloads (64 sequences of up to 2k tokens; 16 x 32k tokens), each
+        # run as its own step of pa_decode_append launches, measured in the same run
+        for wl in ("decode-batched", "decode-long"):
+            log(f"{wl} workload for its decode roofline")
+            cfg_d = WORKLOADS[wl]
+            res_d = run_gpu(cfg_d, args.steps, args.warmup)
+            base_d = W.make_case(cfg_d, values=False)
+            rl, _ = decode_rooflines(res_d, base_d, wl)
+            line[f"roofline_{wl.replace('-', '_')}"] = dict(
+                {"workload": W.CONFIG_NAMES[cfg_d], "layer_copies": res_d["n_layers"],
+                 "step_value": round(res_d["value"], 2), "step_ms": round(res_d["ms_per_step"], 4)},
+                **{k.replace("roofline", "launch"): v for k, v in rl.items()})
     line["append_ms_per_layer"] = round(res["append_ms"], 5)
     line["cpu_baseline"] = dict(cpu, **host_cpu()) if cpu else cpu
     print(json.dumps(line), flush=True)

@@ -289,6 +289,22 @@ def test_prefill_key_groups_and_splits_small_grid(splits, causal):
     assert_close(out, ref, f"small grid kv_splits={splits} causal={causal}")
 
 
+@pytest.mark.parametrize("heads", [(4, 1), (8, 2), (64, 16)])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_prefill_other_head_counts(heads, bs):
+    # one KV head (a tiny grid: two key groups and key pieces), two, and sixteen (a grid of
+    # one key group), over prompts and chunks with cached prefixes
+    hq, hkv = heads
+    case = W.custom_case([300, 37, 129, 64], [300, 20, 65, 1], kind="prefill", block_size=bs,
+                         seed=93 + hq + bs, num_q_heads=hq, num_kv_heads=hkv)
+    _announce(f"prefill heads {hq}/{hkv} bs={bs}")
+    g = GpuCase(case)
+    out = g.prefill()
+    kp, vp = oracle_pools(case)
+    ref = oracle_prefill(case, kp, vp)
+    assert_close(out, ref, f"prefill heads {hq}/{hkv} bs={bs}")
+
+
 @pytest.mark.parametrize("splits", [1, 4])
 def test_prefill_out_of_range_page_gives_nan_rows(splits):
     # a block-table entry outside the pool: exactly the rows whose keys reach that block
