@@ -131,9 +131,6 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x + (row == 0 ? 0 : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
 }
 
-__device__ __forceinline__ float shfl_xor_f(float x, int m) {
-  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, x), m, kWave));
-}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -501,8 +501,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         float a = acc[i][h];
-        a += shfl_xor_f(a, 1);
-        if (LPR == 4) a += shfl_xor_f(a, 2);
+        // the LPR lanes of a dimension are neighbours inside a quad: DPP swaps, no LDS
+        a += dpp_f<kDppQuadSwap1>(a);
+        if (LPR == 4) a += dpp_f<kDppQuadSwap2>(a);
         acc[i][h] = bad ? __builtin_nanf("") : a;
       }
     }
