@@ -322,9 +322,11 @@ int pa_decode_noalloc(pa_geom_t g, void* out, const void* q, const void* k_pool,
  * so a chunk attends to the cached prefix.  Matrix products run on bf16 MFMA with fp32
  * accumulation.  One workgroup per (tile of 32 query rows, sequence, KV head).  When the
  * call has fewer tiles than compute units, a workgroup runs two groups of four waves that
- * take alternate 64-key stages of its tile and merge their results in LDS.  When the
- * grid is still small, each tile's keys are also split into pieces whose fp32 partials
- * (max, sum, unnormalised output) a second kernel merges by log-sum-exp in piece order.
+ * take alternate 64-key stages of its tile and merge their results in LDS; with at most
+ * half as many tiles as compute units, two workgroups share each tile, two query heads
+ * each, and run four key groups that take every fourth stage.  When the grid is still
+ * small, each tile's keys are also split into pieces whose fp32 partials (max, sum,
+ * unnormalised output) a second kernel merges by log-sum-exp in piece order.
  *   out, q      [n_q_tokens][num_q_heads][head_dim] bf16 (device),
  *               n_q_tokens = cu_q_lens[n_seqs]
  *   cu_q_lens   int32 [n_seqs+1] (device); q_len_s <= ctx_lens[s] required
@@ -332,11 +334,11 @@ int pa_decode_noalloc(pa_geom_t g, void* out, const void* q, const void* k_pool,
  *   max_ctx_len host upper bound of ctx_lens (<= max_blocks_per_seq * block_size)
  *   scale       as for pa_decode: finite and > 0
  *   kv_splits   0: automatic, from the T tiles below and the C compute units of the
- *               current device: with T >= C, enough pieces for 2 C workgroups; with
- *               T < C (two key groups per workgroup), enough for C / 2 workgroups; 1 when
- *               T already reaches that, and always at most 8 and at most
- *               ceil(max_ctx_len/64).  Else that many pieces, 1 .. 8.  Other values give
- *               PA_ERR_INVALID_ARG.
+ *               current device, with W = T workgroups per piece (W = 2 T when 2 T <= C):
+ *               with T >= C, enough pieces for 2 C workgroups; with T < C (key groups),
+ *               enough for C / 2 workgroups; 1 when W already reaches that, and always
+ *               at most 8 and at most ceil(max_ctx_len/64).  Else that many pieces,
+ *               1 .. 8.  Other values give PA_ERR_INVALID_ARG.
  *   workspace   device scratch of at least pa_prefill_workspace_bytes(...) bytes for the
  *               same arguments (on the same device); may be NULL when that size is 0.
  *               With T = ceil(max_q_len/32) * n_seqs * num_kv_heads tiles and P pieces

@@ -92,7 +92,8 @@ constexpr int kPrefillMaxSplit = 8;
 struct PrefillPlan {
   int64_t items;    // tiles x sequences x KV heads (the tile grid, ceil(max_q/32) tiles each)
   int split;        // key pieces per tile (1: no merge)
-  int groups;       // key groups per workgroup (1 or 2)
+  int groups;       // key groups per workgroup (1, 2 or 4)
+  int heads;        // query heads per key group (4, or 2 with four key groups)
   size_t ws_bytes;  // partials (0 when split is 1)
 };
 

@@ -10,11 +10,14 @@
 //
 // Work split: one workgroup per (query tile of 32 positions, sequence, KV head); its four
 // waves are the four query heads of that KV head.  Tiles are issued longest first (the
-// highest query positions see the most keys under the causal mask).
+// highest query positions see the most keys under the causal mask).  Small grids give a
+// workgroup G key groups (each a copy of the four waves, taking every G-th stage, merged
+// in LDS at the end), and the smallest split a tile's heads over two workgroups of two
+// head-waves per group with four groups each.
 //
-// K/V stages: the workgroup copies 64 keys of K and V (the pages' own head slices) from
-// HBM into LDS once for all four head-waves, double-buffered: the 256 threads load stage
-// s+1 into registers while the waves compute stage s from LDS, then store it to the other
+// K/V stages: each key group copies 64 keys of K and V (the pages' own head slices) from
+// HBM into LDS once for all its head-waves, double-buffered: its threads load stage s+1
+// into registers while the waves compute stage s from LDS, then store it to the other
 // buffer.  K keeps the page's [8 pieces][bs][8] order (a wave's A-operand reads are then
 // contiguous 512-byte runs); V rows ([64 dims][bs]) are padded by 8 bytes so the 32 rows
 // an MFMA A-operand read touches fall in distinct LDS banks.  V values of keys past the
@@ -41,7 +44,6 @@ namespace {
 
 constexpr int kQTile = 32;   // query positions per workgroup
 constexpr int kStage = 64;   // keys per LDS stage
-constexpr int kThreads = 256;
 constexpr float kLazy = 8.f;  // log2 of the largest p the lazy rescale lets through
 constexpr int kSlotFloats = kGroup * kQTile * kHeadDim;  // one partial output (fp32)
 constexpr int kSlotRows = kGroup * kQTile;               // (max, sum) pairs of one partial
@@ -82,8 +84,9 @@ struct PrefillLds {
   uint16_t v[2][PPS][kHeadDim][VROW];      // [stage][page][dim][bs + pad]
 };
 
-template <int BS, int G>
-__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) void prefill_kernel(
+template <int BS, int G, int HPW>
+__global__ __launch_bounds__(64 * HPW * G) __attribute__((amdgpu_waves_per_eu(HPW == kGroup ? 3 : 2)))
+void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ k_pool, const uint16_t* __restrict__ v_pool,
     const int32_t* __restrict__ block_tables, int max_blocks,
@@ -94,6 +97,10 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
   constexpr int PPS = Lds::PPS;
   constexpr int VROW = Lds::VROW;
   constexpr int KCH = 8 * BS;  // 16-byte chunks of one page's K (or V) head slice
+  constexpr int kGT = 64 * HPW;          // threads of one key group: a wave per query head
+  constexpr int NHP = kGroup / HPW;      // workgroups sharing one tile, by query heads
+  constexpr int NC = kStage * kHeadDim / 8 / kGT;  // 16-byte K (and V) chunks per thread
+  static_assert(NC * kGT * 8 == kStage * kHeadDim && KCH % 64 == 0, "staging");
   __shared__ __attribute__((aligned(16))) Lds sh_all[G];
 
   // Work order: tiles longest first (highest query positions see the most keys), the
@@ -101,24 +108,27 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
   // the XCDs (bid mod 8) and, inside one, to its shader engines in turn; without the
   // rotation a sequence would land on the same engine at every level and the engines'
   // loads would differ by the sequences' lengths.
-  // With n_split > 1 the tile's keys are cut into n_split pieces (pieces of one tile are
-  // n_split * Hkv workgroups apart; the KV head stays bid mod Hkv).
+  // With HPW < 4 the query heads of a tile are shared out over NHP workgroups (Hkv apart,
+  // so on one XCD); with n_split > 1 the tile's keys are also cut into n_split pieces
+  // (NHP * Hkv workgroups apart).  The KV head stays bid mod Hkv.
   const int bid = blockIdx.x;
   const int g = bid % num_kv_heads;
-  const int piece = (bid / num_kv_heads) % n_split;
-  const int tb = bid / (num_kv_heads * n_split);  // tile-level position
+  const int hp = (bid / num_kv_heads) % NHP;
+  const int piece = (bid / (num_kv_heads * NHP)) % n_split;
+  const int tb = bid / (num_kv_heads * NHP * n_split);  // tile-level position
   const int level = tb / n_seqs;
   const int s = (tb % n_seqs + level) % n_seqs;
   const int tile = n_qtiles - 1 - level;
-  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);  // key group
+  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / kGT);  // key group
   Lds& sh = sh_all[grp];
-  const int tid = threadIdx.x & 255;  // thread within the group
+  const int tid = threadIdx.x % kGT;  // thread within the group
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int j = lane & 31;    // query column of this lane
   const int half = lane >> 5;
   const int hq = num_kv_heads * kGroup;
-  const int head = g * kGroup + w;
+  const int hw = hp * HPW + w;  // this wave's query head within the KV head's group
+  const int head = g * kGroup + hw;
 
   const int qa = cu_q_lens[s];
   const int qlen = cu_q_lens[s + 1] - qa;
@@ -157,46 +167,44 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
   const uint16_t* k_head = k_pool + g * head_stride;
   const uint16_t* v_head = v_pool + g * head_stride;
 
-  // ---- staging: thread t moves K chunks t, t+256 and V chunks t, t+256 of a stage ------
+  // ---- staging: thread t moves K and V chunks t + i kGT (i < NC) of a stage ----------
   // chunk c of a stage: page c / KCH, 16-byte piece c % KCH of that page's head slice.
-  // A thread's share of a stage: K and V chunks tid and tid + 256 (16 bytes each).  A
-  // page slice is KCH >= 128 chunks, so each wave's 64 chunks of either kind lie in one
-  // page: block-table entries and page addresses are wave-uniform (scalar registers),
-  // and a lane only adds its byte offset within the page.
+  // A page slice is KCH >= 128 chunks, so each wave's 64 chunks of either kind in one
+  // instruction lie in one page: block-table entries and page addresses are wave-uniform
+  // (scalar registers), and a lane only adds its byte offset within the page.
   struct StageRegs {  // plain vector types: HIP's uint4 copies go through the stack
-    u32x4_t k0, k1, v0, v1;
-    int bad;  // bit 0 / 1: the page of chunk t / t + 256 was out of range (wave-uniform)
+    u32x4_t k[NC], v[NC];
+    int bad;  // bit i: the page of chunk tid + i kGT was out of range (wave-uniform)
   };
-  const int pj_a = (64 * w) / KCH;             // page (within a stage) of chunk tid
-  const int pj_b = (64 * w + kThreads) / KCH;  // and of chunk tid + 256
-  const unsigned off_a = (unsigned)(tid % KCH) * 16u;               // bytes into the page slice
-  const unsigned off_b = (unsigned)((tid + kThreads) % KCH) * 16u;
   const size_t page_bytes = page_stride * sizeof(uint16_t);
   const char* k_base = reinterpret_cast<const char*>(k_head);
   const char* v_base = reinterpret_cast<const char*>(v_head);
-  // Block-table entries of the wave's two pages of stage st, pages past the last needed
-  // block repeating it.
-  auto stage_pids = [&](int st, int& pa, int& pb) __attribute__((always_inline)) {
+  // Block-table entries of the wave's pages of stage st (one per chunk instruction), pages
+  // past the last needed block repeating it.
+  auto stage_pids = [&](int st, int (&pid)[NC]) __attribute__((always_inline)) {
     const int blk0 = st * (kStage / BS);
-    pa = bt[__builtin_amdgcn_readfirstlane(min(blk0 + pj_a, last_blk))];
-    pb = bt[__builtin_amdgcn_readfirstlane(min(blk0 + pj_b, last_blk))];
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      pid[i] = bt[__builtin_amdgcn_readfirstlane(min(blk0 + (64 * w + kGT * i) / KCH, last_blk))];
   };
   // Issue the thread's loads of a stage.  `live` false (a stage past the end) points every
   // lane at the page's first 16 bytes, so each load instruction fetches one line.  A page
   // id out of range reads page 0 instead and marks the chunk, which is staged as K = NaN,
   // V = 0.
-  auto stage_load = [&](StageRegs& r, int pa, int pb, bool live) __attribute__((always_inline)) {
-    pa = __builtin_amdgcn_readfirstlane(pa);
-    pb = __builtin_amdgcn_readfirstlane(pb);
+  auto stage_load = [&](StageRegs& r, const int (&pid)[NC], bool live) __attribute__((always_inline)) {
     r.bad = 0;
-    if ((unsigned)pa >= (unsigned)num_pages) { r.bad |= 1; pa = 0; }
-    if ((unsigned)pb >= (unsigned)num_pages) { r.bad |= 2; pb = 0; }
-    const size_t pga = (size_t)pa * page_bytes, pgb = (size_t)pb * page_bytes;
-    const unsigned oa = live ? off_a : 0u, ob = live ? off_b : 0u;
-    r.k0 = *reinterpret_cast<const u32x4_t*>(k_base + pga + oa);
-    r.v0 = *reinterpret_cast<const u32x4_t*>(v_base + pga + oa);
-    r.k1 = *reinterpret_cast<const u32x4_t*>(k_base + pgb + ob);
-    r.v1 = *reinterpret_cast<const u32x4_t*>(v_base + pgb + ob);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      int pg = __builtin_amdgcn_readfirstlane(pid[i]);
+      if ((unsigned)pg >= (unsigned)num_pages) {
+        r.bad |= 1 << i;
+        pg = 0;
+      }
+      const size_t pgo = (size_t)pg * page_bytes;
+      const unsigned off = live ? (unsigned)((tid + kGT * i) % KCH) * 16u : 0u;
+      r.k[i] = *reinterpret_cast<const u32x4_t*>(k_base + pgo + off);
+      r.v[i] = *reinterpret_cast<const u32x4_t*>(v_base + pgo + off);
+    }
   };
   // V chunk c: dim row within / (BS/8), keys 8 * (within % (BS/8)) .. +8 of page c / KCH;
   // keys at or past the context end are cleared
@@ -222,15 +230,21 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
     if (__builtin_expect(r.bad != 0, 0)) {
       const u32x4_t nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
       const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-      if (r.bad & 1) { r.k0 = nan4; r.v0 = zero4; }
-      if (r.bad & 2) { r.k1 = nan4; r.v1 = zero4; }
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        if (r.bad & (1 << i)) {
+          r.k[i] = nan4;
+          r.v[i] = zero4;
+        }
+      }
     }
     const int k0 = st * kStage;
     const bool tail = k0 + kStage > ctx;  // the stage reaches past the context end
-    *reinterpret_cast<u32x4_t*>(&sh.k[buf][tid * 8]) = r.k0;
-    *reinterpret_cast<u32x4_t*>(&sh.k[buf][(tid + kThreads) * 8]) = r.k1;
-    store_v(k0, tail, tid, r.v0, buf);
-    store_v(k0, tail, tid + kThreads, r.v1, buf);
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      *reinterpret_cast<u32x4_t*>(&sh.k[buf][(tid + kGT * i) * 8]) = r.k[i];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) store_v(k0, tail, tid + kGT * i, r.v[i], buf);
   };
 
   // This lane's query row: reference maximum m (scaled), m + kLazy, the FMA addend -m (0
@@ -414,10 +428,10 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
     // within 32 of its first row, which sits below 63; otherwise the context is shorter
     // than a stage): staged one at a time, without the pipeline.
     for (int u = 0; u < n_u; ++u) {
-      int pa_s, pb_s;
-      stage_pids(stage_of(u), pa_s, pb_s);
+      int pid_s[NC];
+      stage_pids(stage_of(u), pid_s);
       StageRegs r;
-      stage_load(r, pa_s, pb_s, live_of(u));
+      stage_load(r, pid_s, live_of(u));
       stage_store(r, stage_of(u), u & 1);
       __syncthreads();
       if (live_of(u)) compute_stage_precise(u & 1, stage_of(u) * kStage);
@@ -432,14 +446,14 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
     // is unrolled by two with fixed registers per parity, so the compiler's wait counts let
     // the loads of round u + 2 stay in flight across the store of round u + 1.
     StageRegs ra, rb;   // round u lives in ra for even u, rb for odd u
-    int pa_e, pb_e, pa_o, pb_o;  // block-table entries for even / odd rounds
+    int pid_e[NC], pid_o[NC];  // block-table entries for even / odd rounds
     if (n_u > 0) {
-      int p0a, p0b;
-      stage_pids(stage_of(0), p0a, p0b);
-      stage_pids(stage_of(1), pa_o, pb_o);
-      stage_load(ra, p0a, p0b, live_of(0));
-      stage_pids(stage_of(2), pa_e, pb_e);
-      stage_load(rb, pa_o, pb_o, live_of(1));
+      int pid0[NC];
+      stage_pids(stage_of(0), pid0);
+      stage_pids(stage_of(1), pid_o);
+      stage_load(ra, pid0, live_of(0));
+      stage_pids(stage_of(2), pid_e);
+      stage_load(rb, pid_o, live_of(1));
       stage_store(ra, stage_of(0), 0);
     }
     // An explicit use of q here, after the prologue has waited for younger loads: the
@@ -451,11 +465,11 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
       constexpr int P = decltype(parity)::value;
       const int buf = u & 1;
       if constexpr (P == 0) {
-        stage_pids(stage_of(u + 3), pa_o, pb_o);
-        stage_load(ra, pa_e, pb_e, live_of(u + 2));
+        stage_pids(stage_of(u + 3), pid_o);
+        stage_load(ra, pid_e, live_of(u + 2));
       } else {
-        stage_pids(stage_of(u + 3), pa_e, pb_e);
-        stage_load(rb, pa_o, pb_o, live_of(u + 2));
+        stage_pids(stage_of(u + 3), pid_e);
+        stage_load(rb, pid_o, live_of(u + 2));
       }
       if (live_of(u)) compute_stage_fast(buf, stage_of(u) * kStage);
       // Stored on every round, also past the last one (the other buffer is not read
@@ -481,10 +495,11 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
     // accumulators; group 0 combines them, M = max m_g, weights 2^(m_g - M) (0 for a
     // group that saw no key of the row), and goes on with the result alone.
     constexpr int kF = 34;  // floats per lane: o0, o1, m, lsum
+    static_assert((G - 1) * HPW * kF * 64 * sizeof(float) <= sizeof(sh_all), "merge space");
     float* mb = reinterpret_cast<float*>(sh_all);
     __syncthreads();
     if (grp > 0) {
-      float* dst = mb + ((size_t)((grp - 1) * kGroup + w) * kF) * 64 + lane;
+      float* dst = mb + ((size_t)((grp - 1) * HPW + w) * kF) * 64 + lane;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         dst[r * 64] = o0[r];
@@ -498,7 +513,7 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
     float mg[G - 1], M = m;
 #pragma unroll
     for (int k = 1; k < G; ++k) {
-      mg[k - 1] = mb[((size_t)((k - 1) * kGroup + w) * kF + 32) * 64 + lane];
+      mg[k - 1] = mb[((size_t)((k - 1) * HPW + w) * kF + 32) * 64 + lane];
       M = vmax(M, mg[k - 1]);
     }
     const float f0 = m == kNegInf ? 0.f : fast_exp2(m - M);
@@ -510,7 +525,7 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
     }
 #pragma unroll
     for (int k = 1; k < G; ++k) {
-      const float* srcp = mb + ((size_t)((k - 1) * kGroup + w) * kF) * 64 + lane;
+      const float* srcp = mb + ((size_t)((k - 1) * HPW + w) * kF) * 64 + lane;
       const float f = mg[k - 1] == kNegInf ? 0.f : fast_exp2(mg[k - 1] - M);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -525,11 +540,12 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
   if (n_split > 1) {
     // a piece: fp32 partial (reference maximum, sum, unnormalised output) for the merge,
     // slot (item, piece) with item = (tile * n_seqs + s) * Hkv + g, in lane order: wave w's
-    // accumulator chunk r (o0 then o1, 4 floats) of lane l at float (w * 8 + r) * 256 + 4 l,
+    // accumulator chunk r (o0 then o1, 4 floats) of lane l at float (hw * 8 + r) * 256 + 4 l
+    // (hw: the wave's query head within the KV head's group),
     // so every store (and the merge's load) moves one contiguous kilobyte
     const float ltot = pair_sum(lsum);
     const size_t slot = ((size_t)(tile * n_seqs + s) * num_kv_heads + g) * n_split + piece;
-    float* po = ws_o + slot * kSlotFloats + w * 8 * 256 + 4 * lane;
+    float* po = ws_o + slot * kSlotFloats + hw * 8 * 256 + 4 * lane;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       *reinterpret_cast<f32x4_t*>(po + r4 * 256) =
@@ -537,7 +553,7 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(3))) vo
       *reinterpret_cast<f32x4_t*>(po + (4 + r4) * 256) =
           f32x4_t{o1[4 * r4], o1[4 * r4 + 1], o1[4 * r4 + 2], o1[4 * r4 + 3]};
     }
-    if (half == 0) ws_ml[slot * kSlotRows + w * kQTile + j] = make_float2(m, ltot);
+    if (half == 0) ws_ml[slot * kSlotRows + hw * kQTile + j] = make_float2(m, ltot);
     return;
   }
 
@@ -630,15 +646,23 @@ PrefillPlan plan_prefill(int n_seqs, int max_q_len, int max_ctx_len, int num_kv_
   const int64_t cus = std::max(compute_units, 1);
   p.items = items;
   // A grid smaller than the chip gives each tile two key groups (eight waves), halving the
-  // serial stage chain of its workgroup; a larger one keeps three four-wave workgroups
-  // per compute unit.
-  p.groups = items > 0 && items < cus ? 2 : 1;
+  // serial stage chain of its workgroup; at most half the chip, each tile goes to two
+  // workgroups of two query heads with four key groups each (eight waves again, a quarter
+  // of the chain).  A larger grid keeps three four-wave workgroups per compute unit.
+  if (items > 0 && 2 * items <= cus) {
+    p.groups = 4;
+    p.heads = 2;
+  } else {
+    p.groups = items > 0 && items < cus ? 2 : 1;
+    p.heads = kGroup;
+  }
+  const int64_t wgs = items * (kGroup / p.heads);  // workgroups per key piece
   int64_t split = kv_splits;
   if (split == 0) {  // at most 8 pieces, never more than the stages
-    // one-group workgroups: enough for two per compute unit; two-group ones: enough for
+    // one-group workgroups: enough for two per compute unit; several groups: enough for
     // half the compute units (the pieces' merge costs more than the idle units)
-    const int64_t want = p.groups == 2 ? cus / 2 : 2 * cus;
-    split = items > 0 && items < want ? (want + items - 1) / items : 1;
+    const int64_t want = p.groups == 1 ? 2 * cus : cus / 2;
+    split = wgs > 0 && wgs < want ? (want + wgs - 1) / wgs : 1;
     split = std::min<int64_t>(std::min<int64_t>(split, kPrefillMaxSplit), stages);
   }
   p.split = (int)std::max<int64_t>(split, 1);
@@ -654,8 +678,8 @@ hipError_t launch_prefill(const LaunchGeom& geo, const PrefillPlan& plan, void* 
                           hipStream_t stream) {
   const int n_qtiles = (max_q_len + kQTile - 1) / kQTile;
   const int ns = plan.split;
-  const dim3 grid((unsigned)(plan.items * ns));
-  const dim3 block(kThreads * plan.groups);
+  const dim3 grid((unsigned)(plan.items * (kGroup / plan.heads) * ns));
+  const dim3 block(64 * plan.heads * plan.groups);
   const float qk_scale = scale * kLog2e;
   auto* o = static_cast<uint16_t*>(out);
   auto* qq = static_cast<const uint16_t*>(q);
@@ -667,14 +691,18 @@ hipError_t launch_prefill(const LaunchGeom& geo, const PrefillPlan& plan, void* 
     ws_o = static_cast<float*>(workspace);
     ws_ml = reinterpret_cast<float2*>(ws_o + (size_t)plan.items * ns * kSlotFloats);
   }
-#define PA_PREFILL_LAUNCH(B, NG)                                                              \
-  hipLaunchKernelGGL((prefill_kernel<B, NG>), grid, block, 0, stream, o, qq, kp, vp, block_tables, \
-                     max_blocks, cu_q_lens, ctx_lens, n_seqs, n_qtiles, geo.num_pages,            \
-                     geo.num_kv_heads, qk_scale, causal, ns, ws_o, ws_ml)
+#define PA_PREFILL_LAUNCH(B, NG, NH)                                                          \
+  hipLaunchKernelGGL((prefill_kernel<B, NG, NH>), grid, block, 0, stream, o, qq, kp, vp,         \
+                     block_tables, max_blocks, cu_q_lens, ctx_lens, n_seqs, n_qtiles,            \
+                     geo.num_pages, geo.num_kv_heads, qk_scale, causal, ns, ws_o, ws_ml)
   if (geo.block_size == 16) {
-    if (plan.groups == 2) PA_PREFILL_LAUNCH(16, 2); else PA_PREFILL_LAUNCH(16, 1);
+    if (plan.groups == 4) PA_PREFILL_LAUNCH(16, 4, 2);
+    else if (plan.groups == 2) PA_PREFILL_LAUNCH(16, 2, 4);
+    else PA_PREFILL_LAUNCH(16, 1, 4);
   } else {
-    if (plan.groups == 2) PA_PREFILL_LAUNCH(32, 2); else PA_PREFILL_LAUNCH(32, 1);
+    if (plan.groups == 4) PA_PREFILL_LAUNCH(32, 4, 2);
+    else if (plan.groups == 2) PA_PREFILL_LAUNCH(32, 2, 4);
+    else PA_PREFILL_LAUNCH(32, 1, 4);
   }
 #undef PA_PREFILL_LAUNCH
   hipError_t e = hipGetLastError();

@@ -240,8 +240,9 @@ def _prefill_ws(n_seqs, max_q, max_ctx, hkv, splits, cus=256):
     stages = max(1, -(-max_ctx // 64))
     p = splits
     if p == 0:
-        want = cus // 2 if 0 < items < cus else 2 * cus  # two key groups below cus tiles
-        p = -(-want // items) if 0 < items < want else 1
+        want = cus // 2 if 0 < items < cus else 2 * cus  # key groups below cus tiles
+        wgs = 2 * items if 2 * items <= cus else items  # two workgroups per tile at most C/2
+        p = -(-want // wgs) if 0 < wgs < want else 1
         p = min(p, 8, stages)
     p = max(p, 1)
     return 0 if p == 1 else items * p * 4 * 32 * (64 * 4 + 8)

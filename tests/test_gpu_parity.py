@@ -274,19 +274,29 @@ def test_prefill_key_splits(splits, causal):
     assert_close(out, ref, f"prefill kv_splits={splits} causal={causal}")
 
 
+SMALL_GRIDS = {
+    # 160 tiles (fewer than the compute units): two key groups of four head-waves
+    "two-groups": ([70, 33, 129, 1, 640], [7, 33, 100, 1, 96], 32),
+    # 80 tiles (at most half the compute units): two workgroups per tile, two head-waves
+    # per group, four key groups
+    "four-groups": ([70, 33, 129, 1, 640], [7, 33, 60, 1, 50], 16),
+}
+
+
+@pytest.mark.parametrize("grid", sorted(SMALL_GRIDS))
 @pytest.mark.parametrize("splits", [1, 2, 5, 8])
 @pytest.mark.parametrize("causal", [True, False])
-def test_prefill_key_groups_and_splits_small_grid(splits, causal):
-    # fewer tiles than compute units: two key groups per workgroup, merged in LDS, and on
-    # top of that the pieces (a piece of one or two stages leaves the second group idle)
-    case = W.custom_case([70, 33, 129, 1, 640], [7, 33, 100, 1, 96], kind="prefill",
-                         block_size=32, seed=92)
-    _announce(f"prefill small grid kv_splits={splits} causal={causal}")
+def test_prefill_key_groups_and_splits_small_grid(grid, splits, causal):
+    # fewer tiles than compute units: key groups per workgroup, merged in LDS, and on top
+    # of that the pieces (a piece of fewer stages than groups leaves groups idle)
+    ctx, new, bs = SMALL_GRIDS[grid]
+    case = W.custom_case(ctx, new, kind="prefill", block_size=bs, seed=92)
+    _announce(f"prefill small grid {grid} kv_splits={splits} causal={causal}")
     g = GpuCase(case)
     out = g.prefill(causal=causal, kv_splits=splits)
     kp, vp = oracle_pools(case)
     ref = oracle_prefill(case, kp, vp, causal=causal)
-    assert_close(out, ref, f"small grid kv_splits={splits} causal={causal}")
+    assert_close(out, ref, f"small grid {grid} kv_splits={splits} causal={causal}")
 
 
 @pytest.mark.parametrize("heads", [(4, 1), (8, 2), (64, 16)])
