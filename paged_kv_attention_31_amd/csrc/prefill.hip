@@ -19,8 +19,10 @@
 // HBM into LDS once for all its head-waves, double-buffered: its threads load stage s+1
 // into registers while the waves compute stage s from LDS, then store it to the other
 // buffer.  K keeps the page's [8 pieces][bs][8] order (a wave's A-operand reads are then
-// contiguous 512-byte runs); V rows ([64 dims][bs]) are padded by 8 bytes so the 32 rows
-// an MFMA A-operand read touches fall in distinct LDS banks.  V values of keys past the
+// contiguous 512-byte runs).  V rows ([64 dims][bs]) are padded by 16 bytes, so the 16
+// rows one pass of a 16-byte read touches fall in distinct LDS banks, and in every
+// 16-key group the middle two 4-key quads trade places, so each lane's Vt operand (keys
+// 4h .. 4h+3 and 8+4h .. 8+4h+3 of a group) is one aligned 16-byte read.  V values of keys past the
 // context are zeroed while staging, so stale pool bytes (even NaN) never reach P.V.
 //
 // Per wave and per 32 keys the products are computed transposed:
@@ -79,7 +81,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 template <int BS>
 struct PrefillLds {
   static constexpr int PPS = kStage / BS;  // pages per stage
-  static constexpr int VROW = BS + 4;      // padded V row (elements)
+  static constexpr int VROW = BS + 8;      // padded V row (elements, 16-byte aligned)
   uint16_t k[2][kStage * kHeadDim];        // [stage][page][8][bs][8]
   uint16_t v[2][PPS][kHeadDim][VROW];      // [stage][page][dim][bs + pad]
 };
@@ -220,9 +222,11 @@ void prefill_kernel(
         if (key0 + e >= ctx) vv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
       }
     }
-    uint16_t* dst = &sh.v[buf][pj][row][c8 * 8];
+    // within each 16-key group the middle two 4-key quads trade places, so the keys a
+    // Vt operand needs (4h .. 4h+3 and 8+4h .. 8+4h+3) are the 8 contiguous at 8h
+    uint16_t* dst = &sh.v[buf][pj][row][16 * (c8 >> 1) + 4 * (c8 & 1)];
     *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{vv[0], vv[1]};
-    *reinterpret_cast<u32x2_t*>(dst + 4) = u32x2_t{vv[2], vv[3]};
+    *reinterpret_cast<u32x2_t*>(dst + 8) = u32x2_t{vv[2], vv[3]};
   };
   // Rows that see a key of an out-of-range page get NaN scores (and so a NaN output);
   // V = 0 keeps the page's stale values out of the rows that mask those keys.
@@ -342,23 +346,20 @@ void prefill_kernel(
   };
   // O^T += V^T . P^T.  Element e (0..7) of lane half h's B operand for k-step ks is the
   // score of key 16 ks + (e < 4 ? 0 : 8) + 4 h + (e & 3) (the S^T accumulator order), so
-  // the V^T operand reads the two 4-key runs at 16 ks + 4 h and 16 ks + 8 + 4 h.
+  // the V^T operand needs the two 4-key runs at 16 ks + 4 h and 16 ks + 8 + 4 h, which
+  // the staging's quad swap puts next to each other at 16 ks + 8 h.
   struct VOps {
     u32x4_t a[2][2];  // [ks][mb]
   };
   auto read_v = [&](int buf, int hh, VOps& vo) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int kr0 = 32 * hh + 16 * ks + 4 * half;  // first key (within the stage) of run 0
-      const int pj = kr0 / BS;
-      const int slot = kr0 % BS;  // runs at slot and slot + 8 stay inside one page
+      const int kg = 32 * hh + 16 * ks;  // first key (within the stage) of the 16-key group
+      const int pj = kg / BS;
+      const int slot = kg % BS + 8 * half;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const uint16_t* vr = &sh.v[buf][pj][32 * mb + j][slot];
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + 8);
-        vo.a[ks][mb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-      }
+      for (int mb = 0; mb < 2; ++mb)
+        vo.a[ks][mb] = *reinterpret_cast<const u32x4_t*>(&sh.v[buf][pj][32 * mb + j][slot]);
     }
   };
   auto pv = [&](const VOps& vo, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
