@@ -234,11 +234,14 @@ int pa_rope_kv_append(pa_geom_t g, const void* q, void* q_out, const void* k_new
  * token at position ctx_lens[s]-1, attending to all ctx_lens[s] keys (so the token's
  * own K/V must already be appended).  Every (sequence, KV head) pair is streamed once
  * for all query heads of its group with a running max and running sum per head.
- * The work is cut evenly over "workers": the (sequence, KV head) pairs, each a run of
- * ceil(ctx/64) tiles of 64 tokens, are laid end to end and every worker takes an equal
- * contiguous share of tiles, so a pair may be split between workers; each worker then
- * leaves an fp32 partial (max, sum, unnormalised output) in `workspace` and a second
- * kernel merges the partials of split pairs by log-sum-exp in a fixed order.
+ * The work is cut over "workers": the (sequence, KV head) pairs, each a run of
+ * ceil(ctx/64) tiles of 64 tokens, are laid end to end and every worker takes a
+ * contiguous share of tiles: 27 parts for the four waves of an even-numbered workgroup,
+ * 25 for those of an odd one (with fewer than two tiles per worker, equal shares), since
+ * the odd-numbered XCDs stream the loads more slowly.  A pair may be split between
+ * workers; each worker then leaves an fp32 partial (max, sum, unnormalised output) in
+ * `workspace` and a second kernel merges the partials of split pairs by log-sum-exp in a
+ * fixed order.  The cut depends only on the tile count and the worker count.
  *   out, q          [n_seqs][num_q_heads][head_dim] bf16 (device)
  *   ctx_lens        int32 [n_seqs] (device); 0 gives a zero row; values above
  *                   max_ctx_len are treated as max_ctx_len
@@ -247,10 +250,11 @@ int pa_rope_kv_append(pa_geom_t g, const void* q, void* q_out, const void* k_new
  *                   (n_seqs * num_kv_heads * ceil(max_ctx_len/64) < 2^31)
  *   scale           multiplies q.k before the softmax: finite and > 0
  *                   (1/sqrt(head_dim) = 0.125); anything else gives PA_ERR_INVALID_ARG
- *   partition_tokens  0: four workers per compute unit of the current device; else a
- *                   positive multiple of 64, and enough workers that none streams more
- *                   than that many tokens.  Either way no worker takes more than
- *                   56 * num_kv_heads tiles.  Other values give PA_ERR_INVALID_ARG.
+ *   partition_tokens  0: four workers per compute unit of the current device (more if
+ *                   a share would exceed 56 * num_kv_heads tiles); else a positive
+ *                   multiple of 64, and enough workers that none streams more than that
+ *                   many tokens (nor more than 56 * num_kv_heads tiles).  Other values
+ *                   give PA_ERR_INVALID_ARG.
  *   workspace       device scratch of at least pa_decode_workspace_bytes(...) bytes
  *                   for the same arguments (on the same device); may be NULL when that
  *                   size is 0.  With W workers it is 2W * 4 * (64 * 4 + 8) + 8 * (W + 1)

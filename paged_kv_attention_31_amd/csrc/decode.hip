@@ -11,8 +11,8 @@
 // Work split (stream-K).  Every (sequence s, KV head g) pair is a segment of
 // tiles(ctx_s) = ceil(ctx_s / 64) tiles of 64 tokens (an empty context counts one empty
 // tile).  Segments are laid end to end in (s, g) order and the whole tile stream is cut
-// into equal contiguous ranges, one per worker wave, so every wave moves the same
-// number of bytes whatever the length mix.  The prefix sum over the context lengths
+// into contiguous ranges, one per worker wave, sized by the wave's weight (see Split), so
+// the waves' shares do not depend on the length mix.  The prefix sum over the context lengths
 // that this needs is computed on the device by every workgroup (the lengths never go to
 // the host).  A wave streams its range tile by tile, crossing segment boundaries
 // without a pause: the K/V loads of the next tile and the page ids and q of the tile
@@ -75,6 +75,38 @@ namespace {
 constexpr int kTile = 64;  // tokens per tile: one per lane for the scores
 
 __device__ __forceinline__ int tiles_of(int ctx) { return ctx > 0 ? (ctx + kTile - 1) / kTile : 1; }
+
+// The stream's cut into worker ranges.  Workgroups go to the XCDs in turn (workgroup b to
+// XCD b mod 8), and on MI355X the odd-numbered XCDs stream this kernel's loads 7-9%
+// slower than the even ones (per-wave wall-clock stamps, on several boxes and workloads),
+// so with equal ranges the launch ends on the odd XCDs.  A wave of an even workgroup
+// therefore takes kWeightEven parts of the stream and one of an odd workgroup
+// kWeightOdd: range w is [T P(w) / P(E), T P(w + 1) / P(E)) with P the prefix sum of the
+// weights.  With fewer than two tiles per wave the cut is the plain equal one (so no range
+// is empty).  The cut depends on (T, E) only, so the results stay deterministic.
+__host__ __device__ constexpr int64_t split_prefix(int64_t w) {
+  constexpr int64_t kS8 = 4 * (kWeightEven + kWeightOdd);  // one even and one odd workgroup
+  const int64_t r = w % 8;
+  return (w / 8) * kS8 + (r < 4 ? r * kWeightEven : 4 * kWeightEven + (r - 4) * kWeightOdd);
+}
+struct Split {
+  int64_t T;  // tiles in the stream
+  int E;      // worker waves
+  __device__ bool weighted() const { return T >= 2 * (int64_t)E; }
+  __device__ int64_t start(int w) const {
+    return weighted() ? T * split_prefix(w) / split_prefix(E) : (int64_t)w * T / E;
+  }
+  // the range holding tile t: the largest w with start(w) <= t
+  __device__ int holding(int64_t t) const {
+    if (!weighted()) return (int)(((t + 1) * E - 1) / T);
+    constexpr int64_t kS8 = 4 * (kWeightEven + kWeightOdd);
+    const int64_t p = ((t + 1) * split_prefix(E) - 1) / T;  // start(w) <= t <=> P(w) <= p
+    const int64_t w8 = p / kS8, rem = p - w8 * kS8;
+    const int64_t w = 8 * w8 + (rem < 4 * kWeightEven ? rem / kWeightEven
+                                                      : 4 + (rem - 4 * kWeightEven) / kWeightOdd);
+    return (int)min(w, (int64_t)E - 1);
+  }
+};
 
 __device__ __forceinline__ int readlane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 
@@ -185,8 +217,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     if (has_ws && lane == 0) ws_desc[wid] = make_int2(-1, 0);
     return;
   }
-  const int64_t a = (int64_t)wid * n_tiles / n_eff;
-  const int L = (int)((int64_t)(wid + 1) * n_tiles / n_eff - a);
+  const Split split{n_tiles, (int)n_eff};
+  const int64_t a = split.start(wid);
+  const int L = (int)(split.start(wid + 1) - a);
 
   // Chunk holding tile a: the chunk prefix is non-decreasing, so it is the number of chunk
   // starts at or below a, less one (lane l checks chunks 4 l .. 4 l + 3 at once).
@@ -480,9 +513,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   // here, else an fp32 partial.  A range cuts at most two segments, its first (cut at its
   // start) and its last (cut at its end), so wave wid has two partial slots: 2 wid for
   // its first segment, 2 wid + 1 for a last segment whose first tile it holds.  The wave that holds the
-  // first tile of a cut segment (its last segment) records (segment, number of covering
-  // waves) for the merge; wave(t) = floor(((t + 1) * n_eff - 1) / n_tiles) is the range
-  // holding stream tile t.
+  // first tile of a cut segment (its last segment) records (segment, stream index of the
+  // segment's last tile) for the merge, which finds the range holding that tile
+  // (Split::holding).
   // The result goes through LDS so that one 16-byte store per lane writes it (bf16: lane
   // l < 32 holds head l / 8, dims 8 (l % 8) .. +8; fp32: lane l holds head l / 16, dims
   // 4 (l % 16) .. +4), and the stores themselves are issued by the step on every tile
@@ -640,7 +673,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 // Combine the partials of every segment that range boundaries cut.  Wave wid's
 // descriptor names the segment it owns (it holds the segment's first tile) and the
 // stream index of the segment's last tile; with the header (stream length T, waves E)
-// the wave holding that tile is w1 = floor(((last + 1) E - 1) / T), so np = w1 - wid + 1
+// the wave holding that tile is w1 = Split{T, E}.holding(last), so np = w1 - wid + 1
 // consecutive waves left partials for the segment: the owner in its slot 2 wid + 1, each
 // later wave w in its slot 2 w.  M = max_j m_j, L = sum_j l_j 2^(m_j - M),
 // out = sum_j o_j 2^(m_j - M) / L, the sums taken in ascending wave order.  Lane = head
@@ -700,7 +733,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int2 hdr = ws_desc[n_workers];  // (tiles in the stream, workers)
   const int seg = desc.x;
   if (seg < 0) return;
-  const int w_last = (int)((((int64_t)desc.y + 1) * hdr.y - 1) / hdr.x);  // holds tile desc.y
+  const int w_last = Split{hdr.x, hdr.y}.holding(desc.y);  // holds tile desc.y
   const int np = w_last - wid + 1;
   if (np < 2) return;
   const int s = seg / num_kv_heads;
@@ -771,15 +804,26 @@ DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partit
   DecodePlan p{};
   const int64_t tiles_per_seq = std::max<int64_t>(1, ((int64_t)max_ctx_len + kTile - 1) / kTile);
   const int64_t n_max = (int64_t)n_seqs * num_kv_heads * tiles_per_seq;
-  int64_t workers = partition_tokens > 0
-                        ? (n_max + partition_tokens / kTile - 1) / (partition_tokens / kTile)
-                        : (int64_t)kDecodeWaves * std::max(compute_units, 1);
+  // the longest range W workers can get from a stream of at most n_max tiles: an even
+  // workgroup's share of the weighted cut (or, below two tiles per wave, of the equal one)
+  auto longest = [&](int64_t w) {
+    const int64_t equal = (n_max + w - 1) / w;
+    if (n_max < 2 * w) return equal;
+    return std::max(equal, (n_max * kWeightEven + split_prefix(w) - 1) / split_prefix(w));
+  };
   const int64_t max_range = (int64_t)kDecodeMaxSeqsPerRange * num_kv_heads;
-  workers = std::max(workers, (n_max + max_range - 1) / max_range);
+  const int64_t bound = partition_tokens > 0 ? std::min<int64_t>(partition_tokens / kTile, max_range)
+                                             : max_range;
+  int64_t workers = partition_tokens > 0 ? (n_max + bound - 1) / bound
+                                         : (int64_t)kDecodeWaves * std::max(compute_units, 1);
+  // enough workers that no range exceeds the bound: start from the even share's estimate
+  workers = std::max(workers, (n_max * 2 * kWeightEven + bound * (kWeightEven + kWeightOdd) - 1) /
+                                  (bound * (kWeightEven + kWeightOdd)));
   workers = std::max<int64_t>(1, std::min(workers, n_max));
+  while (workers < n_max && longest(workers) > bound) ++workers;
   p.n_max_tiles = n_max;
   p.workers = workers;
-  p.tiles_per_worker = (n_max + workers - 1) / workers;
+  p.tiles_per_worker = std::min(longest(workers), n_max);
   p.merge = workers > 1 && tiles_per_seq > 1;
   if (p.merge) {
     const int64_t slots = 2 * workers;  // two partial slots per worker

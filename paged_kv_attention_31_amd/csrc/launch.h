@@ -50,8 +50,12 @@ hipError_t launch_silu_mul(const void* gate, const void* up, int64_t ld_in, void
                            int64_t ld_out, int n_rows, int width, int compute_units,
                            hipStream_t stream);
 
-// Decode: workgroups of four waves; every wave is one stream-K worker.
+// Decode: workgroups of four waves; every wave is one stream-K worker.  A wave of an
+// even-numbered workgroup takes kWeightEven parts of the tile stream, one of an odd one
+// kWeightOdd (odd XCDs stream the decode loads more slowly).
 constexpr int kDecodeWaves = 4;
+constexpr int64_t kWeightEven = 27;
+constexpr int64_t kWeightOdd = 25;
 // A worker's range is at most this many tiles per KV head (so it touches at most this
 // many sequences plus two, which its lanes can hold).
 constexpr int kDecodeMaxSeqsPerRange = 56;

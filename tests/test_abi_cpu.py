@@ -198,13 +198,38 @@ def test_decode_noalloc_validation_and_scratch_limit(lib):
                            part=64) == _lib.PA_ERR_WORKSPACE
 
 
+WEIGHT_EVEN, WEIGHT_ODD = 27, 25  # a wave's share of the tile stream, even / odd workgroup
+
+
+def _split_prefix(w):
+    r = w % 8
+    return (w // 8) * 4 * (WEIGHT_EVEN + WEIGHT_ODD) + (
+        r * WEIGHT_EVEN if r < 4 else 4 * WEIGHT_EVEN + (r - 4) * WEIGHT_ODD)
+
+
+def _plan_workers(n_seqs, max_ctx, hkv, part, cus=256):
+    """(workers, longest range in tiles) of the documented decode plan."""
+    tiles = max(1, -(-max_ctx // 64))
+    n_max = n_seqs * hkv * tiles
+
+    def longest(w):
+        equal = -(-n_max // w)
+        if n_max < 2 * w:
+            return equal
+        return max(equal, -(-(n_max * WEIGHT_EVEN) // _split_prefix(w)))
+
+    bound = min(part // 64, 56 * hkv) if part else 56 * hkv
+    workers = -(-n_max // bound) if part else 4 * cus
+    workers = max(1, min(workers, n_max))
+    while workers < n_max and longest(workers) > bound:
+        workers += 1
+    return workers, min(longest(workers), n_max)
+
+
 def _plan_ws(n_seqs, max_ctx, hkv, part, cus=256):
     """Workspace bytes of the documented decode plan (no device here: 256 compute units)."""
     tiles = max(1, -(-max_ctx // 64))
-    n_max = n_seqs * hkv * tiles
-    workers = -(-n_max // (part // 64)) if part else 4 * cus
-    workers = max(workers, -(-n_max // (56 * hkv)))
-    workers = max(1, min(workers, n_max))
+    workers, _ = _plan_workers(n_seqs, max_ctx, hkv, part, cus)
     if workers == 1 or tiles == 1:
         return 0
     return 2 * workers * 4 * (64 * 4 + 8) + 8 * (workers + 1)
@@ -217,10 +242,13 @@ def test_partition_choice(lib):
     assert lib.pa_decode_partition_tokens(g, 16, 32768, 320) == 320
     assert lib.pa_decode_partition_tokens(g, 16, 32768, 100) == _lib.PA_ERR_INVALID_ARG
     assert lib.pa_decode_partition_tokens(g, 16, 32768, -64) == _lib.PA_ERR_INVALID_ARG
-    # automatic: 4 workers per compute unit, and never more than 56 tiles per KV head each
-    assert lib.pa_decode_partition_tokens(g, 16, 32768, 0) == 16 * 8 * 512 // 1024 * 64
-    assert lib.pa_decode_partition_tokens(g, 4096, 32768, 0) == 56 * 8 * 64
-    assert lib.pa_decode_partition_tokens(g, 4096, 32768, 1 << 20) == 56 * 8 * 64
+    # automatic: 4 workers per compute unit, and never more than 56 tiles per KV head each;
+    # an even workgroup's wave takes 27 parts of the stream to an odd one's 25
+    assert lib.pa_decode_partition_tokens(g, 16, 32768, 0) == -(-65536 * 27 // (128 * 208)) * 64
+    assert lib.pa_decode_partition_tokens(g, 16, 32768, 0) == _plan_workers(16, 32768, 8, 0)[1] * 64
+    assert lib.pa_decode_partition_tokens(g, 4096, 32768, 0) <= 56 * 8 * 64
+    assert lib.pa_decode_partition_tokens(g, 4096, 32768, 0) == _plan_workers(4096, 32768, 8, 0)[1] * 64
+    assert lib.pa_decode_partition_tokens(g, 4096, 32768, 1 << 20) <= 56 * 8 * 64
     for n, ctx in ((16, 32768), (64, 2048), (128, 8192), (1, 37), (1, 1), (4096, 4096)):
         p = lib.pa_decode_partition_tokens(g, n, ctx, 0)
         assert p > 0 and p % 64 == 0
