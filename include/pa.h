@@ -236,9 +236,10 @@ int pa_rope_kv_append(pa_geom_t g, const void* q, void* q_out, const void* k_new
  * for all query heads of its group with a running max and running sum per head.
  * The work is cut over "workers": the (sequence, KV head) pairs, each a run of
  * ceil(ctx/64) tiles of 64 tokens, are laid end to end and every worker takes a
- * contiguous share of tiles: 27 parts for the four waves of an even-numbered workgroup,
- * 25 for those of an odd one (with fewer than two tiles per worker, equal shares), since
- * the odd-numbered XCDs stream the loads more slowly.  A pair may be split between
+ * contiguous share: 27 parts for the four waves of an even-numbered workgroup, 25 for
+ * those of an odd one, since the odd-numbered XCDs stream the loads more slowly, with
+ * the stream measured in units of two per tile and one per pair (a pair's end costs
+ * about half a tile); with fewer than two tiles per worker, equal shares of tiles.  A pair may be split between
  * workers; each worker then leaves an fp32 partial (max, sum, unnormalised output) in
  * `workspace` and a second kernel merges the partials of split pairs by log-sum-exp in a
  * fixed order.  The cut depends only on the tile count and the worker count.

@@ -76,14 +76,23 @@ constexpr int kTile = 64;  // tokens per tile: one per lane for the scores
 
 __device__ __forceinline__ int tiles_of(int ctx) { return ctx > 0 ? (ctx + kTile - 1) / kTile : 1; }
 
-// The stream's cut into worker ranges.  Workgroups go to the XCDs in turn (workgroup b to
-// XCD b mod 8), and on MI355X the odd-numbered XCDs stream this kernel's loads 7-9%
-// slower than the even ones (per-wave wall-clock stamps, on several boxes and workloads),
-// so with equal ranges the launch ends on the odd XCDs.  A wave of an even workgroup
-// therefore takes kWeightEven parts of the stream and one of an odd workgroup
-// kWeightOdd: range w is [T P(w) / P(E), T P(w + 1) / P(E)) with P the prefix sum of the
-// weights.  With fewer than two tiles per wave the cut is the plain equal one (so no range
-// is empty).  The cut depends on (T, E) only, so the results stay deterministic.
+// The stream's cut into worker ranges.  Two things make equal tile counts unequal work:
+// - Workgroups go to the XCDs in turn (workgroup b to XCD b mod 8), and on MI355X the
+//   odd-numbered XCDs stream this kernel's loads 7-9% slower than the even ones (per-wave
+//   wall-clock stamps, on several boxes and workloads).  A wave of an even workgroup
+//   takes kWeightEven parts of the stream, one of an odd workgroup kWeightOdd.
+// - A segment end costs a wave about half a tile (the cross-lane reductions and the
+//   result's store).  The stream is measured in units: two per tile, one per segment end
+//   (the unit after the segment's last tile), so a wave whose range crosses many short
+//   segments gets fewer tiles.
+// Range w holds the tiles whose first unit u = 2 t + seg (seg: the tile's segment index)
+// lies in [U P(w) / P(E), U P(w + 1) / P(E)), with U = 2 T + S and P the prefix sum of
+// the weights.  A range of three or more units holds a tile, and with at least two tiles
+// per wave every range has three units.  Where segments average 32 tiles or more, their
+// ends hardly matter and the weighted cut counts tiles alone (range w: [T P(w) / P(E),
+// T P(w + 1) / P(E)), at least one tile each), which saves a wave the search for the end
+// of its range.  With fewer than two tiles per wave, the cut is the plain equal split of
+// the tiles.  The cut depends on (T, S, E) only, so the results stay deterministic.
 __host__ __device__ constexpr int64_t split_prefix(int64_t w) {
   constexpr int64_t kS8 = 4 * (kWeightEven + kWeightOdd);  // one even and one odd workgroup
   const int64_t r = w % 8;
@@ -91,16 +100,24 @@ __host__ __device__ constexpr int64_t split_prefix(int64_t w) {
 }
 struct Split {
   int64_t T;  // tiles in the stream
+  int64_t S;  // segments in the stream
   int E;      // worker waves
   __device__ bool weighted() const { return T >= 2 * (int64_t)E; }
+  __device__ bool by_units() const { return weighted() && T < 32 * S; }
+  __device__ int64_t units() const { return 2 * T + S; }
+  // first tile of range w (equal or tile-weighted split)
   __device__ int64_t start(int w) const {
     return weighted() ? T * split_prefix(w) / split_prefix(E) : (int64_t)w * T / E;
   }
-  // the range holding tile t: the largest w with start(w) <= t
-  __device__ int holding(int64_t t) const {
+  // unit-weighted split: first unit of range w
+  __device__ int64_t ustart(int w) const { return units() * split_prefix(w) / split_prefix(E); }
+  // the range holding tile t of segment seg
+  __device__ int holding(int64_t t, int64_t seg) const {
     if (!weighted()) return (int)(((t + 1) * E - 1) / T);
     constexpr int64_t kS8 = 4 * (kWeightEven + kWeightOdd);
-    const int64_t p = ((t + 1) * split_prefix(E) - 1) / T;  // start(w) <= t <=> P(w) <= p
+    const int64_t u = by_units() ? 2 * t + seg : t;      // position in the split's measure
+    const int64_t n = by_units() ? units() : T;
+    const int64_t p = ((u + 1) * split_prefix(E) - 1) / n;  // its range w: P(w) <= p
     const int64_t w8 = p / kS8, rem = p - w8 * kS8;
     const int64_t w = 8 * w8 + (rem < 4 * kWeightEven ? rem / kWeightEven
                                                       : 4 + (rem - 4 * kWeightEven) / kWeightOdd);
@@ -118,6 +135,7 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+
 
 // A position in a wave's tile stream (wave-uniform values).
 struct Cursor {
@@ -217,52 +235,90 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     if (has_ws && lane == 0) ws_desc[wid] = make_int2(-1, 0);
     return;
   }
-  const Split split{n_tiles, (int)n_eff};
-  const int64_t a = split.start(wid);
-  const int L = (int)(split.start(wid + 1) - a);
-
-  // Chunk holding tile a: the chunk prefix is non-decreasing, so it is the number of chunk
-  // starts at or below a, less one (lane l checks chunks 4 l .. 4 l + 3 at once).
-  int n_le = 0;
+  const Split split{n_tiles, (int64_t)n_seqs * hkv, (int)n_eff};
+  const bool units = split.by_units();
+  // Position lookup: a position counts tiles (equal split) or units (weighted split).  The
+  // sequences before sequence k, holding cum tiles per KV head, span hkv * cum tiles or
+  // hkv * (2 cum + k) units.
+  auto seq_pos = [&](int64_t cum, int64_t k) -> int64_t {
+    return units ? (int64_t)hkv * (2 * cum + k) : (int64_t)hkv * cum;
+  };
+  struct Where {
+    int s;       // sequence holding the position
+    int code;    // its context-length code
+    int nt;      // its tiles per KV head
+    int64_t cum; // tiles per KV head before it
+  };
+  auto find = [&](int64_t pos) -> Where {
+    // The chunk holding pos: the chunk prefix is non-decreasing, so it is the number of
+    // chunk starts at or below pos, less one (lane l checks chunks 4 l .. 4 l + 3 at once).
+    int n_le = 0;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj)
-    n_le += __popcll(__ballot((int64_t)scan_sh[4 * lane + jj] * hkv <= a));
-  const int lo = uni(n_le) - 1;
-  Cursor cc{-1, 0, 0, 0, 1, 0, false};
-  int64_t cum = uni(scan_sh[lo]);
-  if (chunk == 1) {  // a chunk is one sequence: tile a lies in sequence lo
-    const int code = uni(ctx_sh[lo]);
-    cc.s = lo;
-    cc.ctx = min(code, ctx_cap);
-    cc.over = code > ctx_cap;
-    cc.nt = tiles_of(cc.ctx);
-  }
-  // else the sequence inside the chunk, 64 sequences per step
-  for (int s0 = lo * chunk; cc.s < 0 && s0 < n_seqs; s0 += 64) {
-    const int sj = s0 + lane;
-    const int cj = sj < n_seqs ? (ctx_cached ? ctx_sh[sj] : ctx_code(ctx_lens[sj])) : 0;
-    const int nj = sj < n_seqs ? tiles_of(min(cj, ctx_cap)) : 0;
-    const int pre = wave_incl_scan(nj, lane);
-    const uint64_t hit = __ballot(a < (int64_t)hkv * (cum + pre));
-    if (hit) {
-      const int j = __ffsll((unsigned long long)hit) - 1;
-      cc.s = s0 + j;
-      const int code = readlane_i(cj, j);
-      cc.ctx = min(code, ctx_cap);
-      cc.over = code > ctx_cap;
-      cc.nt = readlane_i(nj, j);
-      cum += readlane_i(pre - nj, j);
-      break;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int c = 4 * lane + jj;
+      n_le += __popcll(__ballot(seq_pos(scan_sh[c], min(c * chunk, n_seqs)) <= pos));
     }
-    cum += readlane_i(pre, 63);
+    const int lo = uni(n_le) - 1;
+    Where wh{-1, 0, 1, uni(scan_sh[lo])};
+    if (chunk == 1) {  // a chunk is one sequence: pos lies in sequence lo
+      wh.s = lo;
+      wh.code = uni(ctx_sh[lo]);
+      wh.nt = tiles_of(min(wh.code, ctx_cap));
+    }
+    // else the sequence inside the chunk, 64 sequences per step
+    for (int s0 = lo * chunk; wh.s < 0 && s0 < n_seqs; s0 += 64) {
+      const int sj = s0 + lane;
+      const int cj = sj < n_seqs ? (ctx_cached ? ctx_sh[sj] : ctx_code(ctx_lens[sj])) : 0;
+      const int nj = sj < n_seqs ? tiles_of(min(cj, ctx_cap)) : 0;
+      const int pre = wave_incl_scan(nj, lane);
+      const uint64_t hit = __ballot(pos < seq_pos(wh.cum + pre, sj + 1));
+      if (hit) {
+        const int j = __ffsll((unsigned long long)hit) - 1;
+        wh.s = s0 + j;
+        wh.code = readlane_i(cj, j);
+        wh.nt = readlane_i(nj, j);
+        wh.cum += readlane_i(pre - nj, j);
+        break;
+      }
+      wh.cum += readlane_i(pre, 63);
+    }
+    return wh;
+  };
+  // (KV head, tile) of position pos inside sequence wh; with units, a position inside a
+  // tile's second unit or on a segment's end unit moves to the next tile (which may be
+  // the next segment's first, i == nt)
+  auto place = [&](const Where& wh, int64_t pos, int& g, int& i) {
+    const int64_t off = pos - seq_pos(wh.cum, wh.s);
+    if (units) {
+      const int64_t segu = 2 * (int64_t)wh.nt + 1;
+      g = (int)(off / segu);
+      i = (int)((off - g * segu + 1) >> 1);
+    } else {
+      g = (int)(off / wh.nt);
+      i = (int)(off - (int64_t)g * wh.nt);
+    }
+  };
+  const int64_t pa = units ? split.ustart(wid) : split.start(wid);
+  const Where wa = find(pa);
+  if (wa.s < 0) return;  // unreachable: a position below the end lies in some sequence
+  int ga, ia;
+  place(wa, pa, ga, ia);
+  const int64_t a = (int64_t)hkv * wa.cum + (int64_t)ga * wa.nt + ia;  // first tile
+  int64_t b = split.start(wid + 1);                                    // one past the last
+  if (units) {
+    const int64_t pb = split.ustart(wid + 1);
+    b = n_tiles;
+    if (pb < split.units()) {
+      const Where wb = find(pb);
+      int gb, ib;
+      place(wb, pb, gb, ib);
+      b = (int64_t)hkv * wb.cum + (int64_t)gb * wb.nt + ib;
+    }
   }
-  if (cc.s < 0) return;  // unreachable: tile a < n_tiles lies in some sequence
-  {
-    cc.first = (int64_t)hkv * cum;
-    const int off = (int)(a - cc.first);
-    cc.g = off / cc.nt;
-    cc.i = off - cc.g * cc.nt;
-  }
+  const int L = (int)(b - a);
+  Cursor cc{wa.s, ga, ia, min(wa.code, ctx_cap), wa.nt, (int64_t)hkv * wa.cum, wa.code > ctx_cap};
+  const bool bump = ia == wa.nt;  // the first tile is the next segment's: step onto it below
+  if (bump) cc.i = wa.nt - 1;
   // Context lengths of the next 64 sequences, one per lane.  A range is at most 56 * Hkv
   // tiles long (the host sizes the worker count for that) and every sequence holds at
   // least Hkv tiles, so a range touches at most 58 sequences.
@@ -285,6 +341,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
       }
     }
   };
+
+  if (bump) advance(cc);
 
   const size_t head_stride = (size_t)kHeadDim * BS;  // elements of one (page, head)
   const size_t page_stride = head_stride * hkv;
@@ -733,7 +791,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int2 hdr = ws_desc[n_workers];  // (tiles in the stream, workers)
   const int seg = desc.x;
   if (seg < 0) return;
-  const int w_last = Split{hdr.x, hdr.y}.holding(desc.y);  // holds tile desc.y
+  const int w_last = Split{hdr.x, (int64_t)n_seqs * num_kv_heads, hdr.y}.holding(desc.y, seg);
   const int np = w_last - wid + 1;
   if (np < 2) return;
   const int s = seg / num_kv_heads;
@@ -805,11 +863,15 @@ DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partit
   const int64_t tiles_per_seq = std::max<int64_t>(1, ((int64_t)max_ctx_len + kTile - 1) / kTile);
   const int64_t n_max = (int64_t)n_seqs * num_kv_heads * tiles_per_seq;
   // the longest range W workers can get from a stream of at most n_max tiles: an even
-  // workgroup's share of the weighted cut (or, below two tiles per wave, of the equal one)
+  // workgroup's share of the weighted cut (units: two per tile, one per segment; r units
+  // hold at most (r + 1) / 2 tiles), or below two tiles per wave of the equal one
+  const int64_t u_max = 2 * n_max + (int64_t)n_seqs * num_kv_heads;
   auto longest = [&](int64_t w) {
     const int64_t equal = (n_max + w - 1) / w;
     if (n_max < 2 * w) return equal;
-    return std::max(equal, (n_max * kWeightEven + split_prefix(w) - 1) / split_prefix(w));
+    const int64_t r = (u_max * kWeightEven + split_prefix(w) - 1) / split_prefix(w);
+    const int64_t t = (n_max * kWeightEven + split_prefix(w) - 1) / split_prefix(w);
+    return std::max(std::max(equal, t), (r + 1) / 2);  // whichever weighted cut applies
   };
   const int64_t max_range = (int64_t)kDecodeMaxSeqsPerRange * num_kv_heads;
   const int64_t bound = partition_tokens > 0 ? std::min<int64_t>(partition_tokens / kTile, max_range)
@@ -817,7 +879,7 @@ DecodePlan plan_decode(int n_seqs, int max_ctx_len, int num_kv_heads, int partit
   int64_t workers = partition_tokens > 0 ? (n_max + bound - 1) / bound
                                          : (int64_t)kDecodeWaves * std::max(compute_units, 1);
   // enough workers that no range exceeds the bound: start from the even share's estimate
-  workers = std::max(workers, (n_max * 2 * kWeightEven + bound * (kWeightEven + kWeightOdd) - 1) /
+  workers = std::max(workers, (u_max * kWeightEven + bound * (kWeightEven + kWeightOdd) - 1) /
                                   (bound * (kWeightEven + kWeightOdd)));
   workers = std::max<int64_t>(1, std::min(workers, n_max));
   while (workers < n_max && longest(workers) > bound) ++workers;

@@ -212,14 +212,18 @@ def _plan_workers(n_seqs, max_ctx, hkv, part, cus=256):
     tiles = max(1, -(-max_ctx // 64))
     n_max = n_seqs * hkv * tiles
 
+    u_max = 2 * n_max + n_seqs * hkv  # units: two per tile, one per segment
+
     def longest(w):
         equal = -(-n_max // w)
         if n_max < 2 * w:
             return equal
-        return max(equal, -(-(n_max * WEIGHT_EVEN) // _split_prefix(w)))
+        tiles = -(-(n_max * WEIGHT_EVEN) // _split_prefix(w))
+        return max(equal, tiles, (-(-(u_max * WEIGHT_EVEN) // _split_prefix(w)) + 1) // 2)
 
     bound = min(part // 64, 56 * hkv) if part else 56 * hkv
     workers = -(-n_max // bound) if part else 4 * cus
+    workers = max(workers, -(-(u_max * WEIGHT_EVEN) // (bound * (WEIGHT_EVEN + WEIGHT_ODD))))
     workers = max(1, min(workers, n_max))
     while workers < n_max and longest(workers) > bound:
         workers += 1
@@ -244,7 +248,7 @@ def test_partition_choice(lib):
     assert lib.pa_decode_partition_tokens(g, 16, 32768, -64) == _lib.PA_ERR_INVALID_ARG
     # automatic: 4 workers per compute unit, and never more than 56 tiles per KV head each;
     # an even workgroup's wave takes 27 parts of the stream to an odd one's 25
-    assert lib.pa_decode_partition_tokens(g, 16, 32768, 0) == -(-65536 * 27 // (128 * 208)) * 64
+    assert lib.pa_decode_partition_tokens(g, 16, 32768, 0) == (-(-(2 * 65536 + 128) * 27 // (128 * 208)) + 1) // 2 * 64
     assert lib.pa_decode_partition_tokens(g, 16, 32768, 0) == _plan_workers(16, 32768, 8, 0)[1] * 64
     assert lib.pa_decode_partition_tokens(g, 4096, 32768, 0) <= 56 * 8 * 64
     assert lib.pa_decode_partition_tokens(g, 4096, 32768, 0) == _plan_workers(4096, 32768, 8, 0)[1] * 64
