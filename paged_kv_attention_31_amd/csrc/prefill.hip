@@ -15,15 +15,17 @@
 // in LDS at the end), and the smallest split a tile's heads over two workgroups of two
 // head-waves per group with four groups each.
 //
-// K/V stages: each key group copies 64 keys of K and V (the pages' own head slices) from
-// HBM into LDS once for all its head-waves, double-buffered: its threads load stage s+1
-// into registers while the waves compute stage s from LDS, then store it to the other
-// buffer.  K keeps the page's [8 pieces][bs][8] order (a wave's A-operand reads are then
-// contiguous 512-byte runs).  V rows ([64 dims][bs]) are padded by 16 bytes, so the 16
-// rows one pass of a 16-byte read touches fall in distinct LDS banks, and in every
-// 16-key group the middle two 4-key quads trade places, so each lane's Vt operand (keys
-// 4h .. 4h+3 and 8+4h .. 8+4h+3 of a group) is one aligned 16-byte read.  V values of keys past the
-// context are zeroed while staging, so stale pool bytes (even NaN) never reach P.V.
+// K/V stages: each key group copies 64 keys of K and V (the pages' own head slices)
+// from the pools straight into LDS (global_load_lds: no staging registers, no LDS store
+// instructions), once for all its head-waves, double-buffered: the copies of stage s+1 fly
+// while the waves compute stage s.  K keeps the page's [8 pieces][bs][8] order (a wave's
+// A-operand reads are then contiguous 512-byte runs).  V keeps the page's [64 dims][bs]
+// rows with their 16-byte units XOR-swizzled by row, so the 16 rows one pass of a 16-byte
+// read touches fall in distinct LDS banks.  Each half's S^T rows hold their keys in an
+// order with bits 2 and 3 of the key swapped, which makes the 8 keys of each lane's V^T
+// operand consecutive: one aligned 16-byte read.  After a copy lands, a wave zeroes the V
+// values of keys past the context in the chunks it copied, so stale pool bytes (even NaN)
+// never reach P.V.
 //
 // Per wave and per 32 keys the products are computed transposed:
 //   S^T[key][query]  = K . Q^T    A = K rows from LDS, B = Q^T (registers, loaded once);
@@ -80,11 +82,21 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 template <int BS>
 struct PrefillLds {
-  static constexpr int PPS = kStage / BS;  // pages per stage
-  static constexpr int VROW = BS + 8;      // padded V row (elements, 16-byte aligned)
-  uint16_t k[2][kStage * kHeadDim];        // [stage][page][8][bs][8]
-  uint16_t v[2][PPS][kHeadDim][VROW];      // [stage][page][dim][bs + pad]
+  uint16_t k[2][kStage * kHeadDim];  // [buffer][page][8][bs][8]: the pages' own order
+  uint16_t v[2][kStage * kHeadDim];  // [buffer][page][dim][bs], 16-byte units swizzled
 };
+// V rows in LDS: the 16-byte units (8 keys) of dim row r sit at unit position u ^ vswz(r),
+// so the 16 rows one pass of a 16-byte read touches fall in distinct LDS banks.
+template <int BS>
+__device__ __forceinline__ int vswz(int row) {
+  return BS == 16 ? (row >> 3) & 1 : (row >> 2) & 3;
+}
+// Wait until this wave's copies into LDS have landed (vector-memory count 0; the compiler
+// does not count these copies itself), and keep memory accesses from moving above it.
+__device__ __forceinline__ void wait_copies() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt free
+  asm volatile("" ::: "memory");
+}
 
 template <int BS, int G, int HPW>
 __global__ __launch_bounds__(64 * HPW * G) __attribute__((amdgpu_waves_per_eu(HPW == kGroup ? 3 : 2)))
@@ -96,8 +108,6 @@ void prefill_kernel(
     int n_qtiles, int num_pages, int num_kv_heads, float qk_scale, int causal, int n_split,
     float* __restrict__ ws_o, float2* __restrict__ ws_ml) {
   using Lds = PrefillLds<BS>;
-  constexpr int PPS = Lds::PPS;
-  constexpr int VROW = Lds::VROW;
   constexpr int KCH = 8 * BS;  // 16-byte chunks of one page's K (or V) head slice
   constexpr int kGT = 64 * HPW;          // threads of one key group: a wave per query head
   constexpr int NHP = kGroup / HPW;      // workgroups sharing one tile, by query heads
@@ -169,15 +179,11 @@ void prefill_kernel(
   const uint16_t* k_head = k_pool + g * head_stride;
   const uint16_t* v_head = v_pool + g * head_stride;
 
-  // ---- staging: thread t moves K and V chunks t + i kGT (i < NC) of a stage ----------
+  // ---- staging: 16-byte chunks c of a stage, copied from the pools straight into LDS ---
   // chunk c of a stage: page c / KCH, 16-byte piece c % KCH of that page's head slice.
   // A page slice is KCH >= 128 chunks, so each wave's 64 chunks of either kind in one
   // instruction lie in one page: block-table entries and page addresses are wave-uniform
   // (scalar registers), and a lane only adds its byte offset within the page.
-  struct StageRegs {  // plain vector types: HIP's uint4 copies go through the stack
-    u32x4_t k[NC], v[NC];
-    int bad;  // bit i: the page of chunk tid + i kGT was out of range (wave-uniform)
-  };
   const size_t page_bytes = page_stride * sizeof(uint16_t);
   const char* k_base = reinterpret_cast<const char*>(k_head);
   const char* v_base = reinterpret_cast<const char*>(v_head);
@@ -189,73 +195,74 @@ void prefill_kernel(
     for (int i = 0; i < NC; ++i)
       pid[i] = bt[__builtin_amdgcn_readfirstlane(min(blk0 + (64 * w + kGT * i) / KCH, last_blk))];
   };
-  // Issue the thread's loads of a stage.  `live` false (a stage past the end) points every
-  // lane at the page's first 16 bytes, so each load instruction fetches one line.  A page
-  // id out of range reads page 0 instead and marks the chunk, which is staged as K = NaN,
-  // V = 0.
-  auto stage_load = [&](StageRegs& r, const int (&pid)[NC], bool live) __attribute__((always_inline)) {
-    r.bad = 0;
+  // Instruction i of wave w fills LDS chunks c0 .. c0 + 63, c0 = 64 (w + HPW i), of the K
+  // and of the V buffer (lane l writes chunk c0 + l: the copy's LDS address is the
+  // instruction's base plus 16 bytes per lane).  K chunks keep the page's order; lane l of
+  // a V instruction fetches the page's unit that belongs at its swizzled position.
+  // Returns the bits of the instructions whose page id was out of range (page 0 was
+  // read instead; stage_fix overwrites those chunks).
+  auto stage_dma = [&](int buf, const int (&pid)[NC]) __attribute__((always_inline)) -> int {
+    int bad = 0;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       int pg = __builtin_amdgcn_readfirstlane(pid[i]);
       if ((unsigned)pg >= (unsigned)num_pages) {
-        r.bad |= 1 << i;
+        bad |= 1 << i;
         pg = 0;
       }
+      const int c0 = 64 * (w + HPW * i);
+      const int within = c0 % KCH + lane;  // chunk within the page slice
+      const int row = within / (BS / 8);
+      const int u = (within % (BS / 8)) ^ vswz<BS>(row);
       const size_t pgo = (size_t)pg * page_bytes;
-      const unsigned off = live ? (unsigned)((tid + kGT * i) % KCH) * 16u : 0u;
-      r.k[i] = *reinterpret_cast<const u32x4_t*>(k_base + pgo + off);
-      r.v[i] = *reinterpret_cast<const u32x4_t*>(v_base + pgo + off);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(k_base + pgo + (size_t)within * 16),
+          (__attribute__((address_space(3))) void*)&sh.k[buf][c0 * 8], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(v_base + pgo +
+                                                           (size_t)(row * (BS / 8) + u) * 16),
+          (__attribute__((address_space(3))) void*)&sh.v[buf][c0 * 8], 16, 0, 0);
     }
+    return bad;
   };
-  // V chunk c: dim row within / (BS/8), keys 8 * (within % (BS/8)) .. +8 of page c / KCH;
-  // keys at or past the context end are cleared
-  auto store_v = [&](int k0, bool tail, int c, u32x4_t vv, int buf) __attribute__((always_inline)) {
-    const int pj = c / KCH;
-    const int within = c - pj * KCH;
-    const int row = within / (BS / 8);
-    const int c8 = within - row * (BS / 8);
-    if (__builtin_expect(tail, 0)) {  // uniform: only the stage holding the context end
-      const int key0 = k0 + pj * BS + c8 * 8;
+  // After this wave's copies of a stage have landed: its chunks from an out-of-range page
+  // become K = NaN, V = 0, and V values of keys at or past the context end become 0 (stale
+  // pool bytes, even NaN, must not meet a zero probability in P.V).  Each lane touches only
+  // the chunks it copied itself, so the stage barrier that follows publishes both.
+  auto stage_fix = [&](int st, int buf, int bad) __attribute__((always_inline)) {
+    const int k0 = st * kStage;
+    const bool tail = k0 + kStage > ctx;
+    if (__builtin_expect(bad == 0 && !tail, 1)) return;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (key0 + e >= ctx) vv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-      }
-    }
-    // within each 16-key group the middle two 4-key quads trade places, so the keys a
-    // Vt operand needs (4h .. 4h+3 and 8+4h .. 8+4h+3) are the 8 contiguous at 8h
-    uint16_t* dst = &sh.v[buf][pj][row][16 * (c8 >> 1) + 4 * (c8 & 1)];
-    *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{vv[0], vv[1]};
-    *reinterpret_cast<u32x2_t*>(dst + 8) = u32x2_t{vv[2], vv[3]};
-  };
-  // Rows that see a key of an out-of-range page get NaN scores (and so a NaN output);
-  // V = 0 keeps the page's stale values out of the rows that mask those keys.
-  auto stage_store = [&](StageRegs& r, int st, int buf) __attribute__((always_inline)) {
-    if (__builtin_expect(r.bad != 0, 0)) {
-      const u32x4_t nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-      const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+    for (int i = 0; i < NC; ++i) {
+      const int c = 64 * (w + HPW * i) + lane;
+      u32x4_t* kd = reinterpret_cast<u32x4_t*>(&sh.k[buf][c * 8]);
+      u32x4_t* vd = reinterpret_cast<u32x4_t*>(&sh.v[buf][c * 8]);
+      if (bad & (1 << i)) {
+        *kd = u32x4_t{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+        *vd = u32x4_t{0u, 0u, 0u, 0u};
+      } else if (tail) {
+        const int pj = c / KCH;
+        const int within = c % KCH;
+        const int row = within / (BS / 8);
+        const int u = (within % (BS / 8)) ^ vswz<BS>(row);
+        const int key0 = k0 + pj * BS + 8 * u;
+        if (key0 + 8 > ctx) {
+          u32x4_t vv = *vd;
 #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        if (r.bad & (1 << i)) {
-          r.k[i] = nan4;
-          r.v[i] = zero4;
+          for (int e = 0; e < 8; ++e)
+            if (key0 + e >= ctx) vv[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          *vd = vv;
         }
       }
     }
-    const int k0 = st * kStage;
-    const bool tail = k0 + kStage > ctx;  // the stage reaches past the context end
-#pragma unroll
-    for (int i = 0; i < NC; ++i)
-      *reinterpret_cast<u32x4_t*>(&sh.k[buf][(tid + kGT * i) * 8]) = r.k[i];
-#pragma unroll
-    for (int i = 0; i < NC; ++i) store_v(k0, tail, tid + kGT * i, r.v[i], buf);
   };
 
   // This lane's query row: reference maximum m (scaled), m + kLazy, the FMA addend -m (0
   // while m is -inf, so masked scores give 2^-inf = 0), and the running sum.
   float m = kNegInf, mthr = kNegInf, negm = 0.f, lsum = 0.f;  // mthr: raw-score units
   const float inv_scale = 1.f / qk_scale;
-  const int lim_lane = klim - 4 * half;  // key offsets from a half's base below this are visible
+  const int lim_lane = klim - 8 * half;  // key offsets from a half's base below this are visible
   f32x16_t o0 = {}, o1 = {};
 
   // A stage is two 32-key halves.  Per half: S^T = K . Q^T (4 MFMAs), the online-softmax
@@ -266,8 +273,12 @@ void prefill_kernel(
   struct KOps {
     u32x4_t a[4];
   };
+  // Row j of a half's S^T holds key sig(j): bits 2 and 3 of j trade places.  The P^T operand
+  // then carries keys 16 ks + 8 h .. 16 ks + 8 h + 7 in lane half h, eight keys in a row, so
+  // the V^T operand is one 16-byte unit.
+  const int sig_j = (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
   auto read_k = [&](int buf, int hh, KOps& ko) __attribute__((always_inline)) {
-    const int kk = 32 * hh + j;  // key within the stage held as A row by this lane
+    const int kk = 32 * hh + sig_j;  // key within the stage held as A row by this lane
     const uint16_t* krow =
         &sh.k[buf][(kk / BS) * (KCH * 8) + (kk % BS) * 8 + half * BS * 8];
 #pragma unroll
@@ -288,10 +299,12 @@ void prefill_kernel(
     constexpr bool PRECISE = decltype(precise_tag)::value;
     float sv[16];
     if ((kb + 32 > ctx) || (causal && kb + 31 > pos_first)) {  // the half crosses a limit
-      // element r is key kb + 8 (r / 4) + 4 half + r % 4, visible while below klim
+      // element r is row 8 (r / 4) + 4 half + r % 4 of S^T, which holds key
+      // kb + 16 (r / 8) + 8 half + 4 ((r / 4) % 2) + r % 4; visible while below klim
       const int lim = lim_lane - kb;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] = (8 * (r >> 2) + (r & 3)) < lim ? sacc[r] : kNegInf;
+      for (int r = 0; r < 16; ++r)
+        sv[r] = (16 * (r >> 3) + 4 * ((r >> 2) & 1) + (r & 3)) < lim ? sacc[r] : kNegInf;
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sv[r] = sacc[r];
@@ -344,22 +357,25 @@ void prefill_kernel(
       for (int i = 0; i < 8; ++i) lsum = dot2(pk[i], 0x3F803F80u, lsum);
     }
   };
-  // O^T += V^T . P^T.  Element e (0..7) of lane half h's B operand for k-step ks is the
-  // score of key 16 ks + (e < 4 ? 0 : 8) + 4 h + (e & 3) (the S^T accumulator order), so
-  // the V^T operand needs the two 4-key runs at 16 ks + 4 h and 16 ks + 8 + 4 h, which
-  // the staging's quad swap puts next to each other at 16 ks + 8 h.
+  // O^T += V^T . P^T.  Element e (0..7) of lane half h's B operand for k-step ks is S^T
+  // row 16 ks + 8 (e / 4) + 4 h + e % 4 (the accumulator order), which holds key
+  // 16 ks + 8 h + e (the rows' key order above), so the V^T operand is the 8 keys from
+  // 16 ks + 8 h: one 16-byte unit of a V row.
   struct VOps {
     u32x4_t a[2][2];  // [ks][mb]
   };
   auto read_v = [&](int buf, int hh, VOps& vo) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int kg = 32 * hh + 16 * ks;  // first key (within the stage) of the 16-key group
+      const int kg = 32 * hh + 16 * ks + 8 * half;  // first of the lane's 8 keys (in the stage)
       const int pj = kg / BS;
-      const int slot = kg % BS + 8 * half;
+      const int u = (kg % BS) / 8;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        vo.a[ks][mb] = *reinterpret_cast<const u32x4_t*>(&sh.v[buf][pj][32 * mb + j][slot]);
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = 32 * mb + j;
+        vo.a[ks][mb] = *reinterpret_cast<const u32x4_t*>(
+            &sh.v[buf][(pj * kHeadDim + row) * BS + 8 * (u ^ vswz<BS>(row))]);
+      }
     }
   };
   auto pv = [&](const VOps& vo, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
@@ -424,70 +440,54 @@ void prefill_kernel(
   const int n_u = (n_stages + G - 1) / G;
   auto stage_of = [&](int u) __attribute__((always_inline)) { return st0 + grp + G * u; };
   auto live_of = [&](int u) __attribute__((always_inline)) { return grp + G * u < n_stages; };
+  // Both paths stage round by round: a wave's copies of a round go straight into LDS, the
+  // wave waits for them (wait_copies), patches its own chunks (stage_fix), and the
+  // workgroup barrier publishes the round.  No copy is issued for a round past the
+  // group's last, and none is in flight when a wave leaves its loop.
   if (__builtin_expect(precise, 0)) {
     // A tile with rows that see few keys has at most two stages (causal: its keys end
     // within 32 of its first row, which sits below 63; otherwise the context is shorter
     // than a stage): staged one at a time, without the pipeline.
     for (int u = 0; u < n_u; ++u) {
-      int pid_s[NC];
-      stage_pids(stage_of(u), pid_s);
-      StageRegs r;
-      stage_load(r, pid_s, live_of(u));
-      stage_store(r, stage_of(u), u & 1);
+      int bad = 0;
+      if (live_of(u)) {
+        int pid_s[NC];
+        stage_pids(stage_of(u), pid_s);
+        bad = stage_dma(u & 1, pid_s);
+      }
+      wait_copies();
+      if (live_of(u)) stage_fix(stage_of(u), u & 1, bad);
       __syncthreads();
       if (live_of(u)) compute_stage_precise(u & 1, stage_of(u) * kStage);
     }
   } else {
-    // Stage pipeline (in rounds).  At round u: LDS buffer u % 2 holds the group's stage of
-    // round u, the registers of round u + 1 are in flight (issued a round ago), and the
-    // block-table entries of round u + 2 have arrived.  The round issues the block-table
-    // loads of round u + 3 and the K/V loads of round u + 2, computes round u from LDS,
-    // stores round u + 1 to the other buffer and meets the barrier.  Every load is issued
-    // unconditionally (stages past the end are the cheap `live = false` kind) and the loop
-    // is unrolled by two with fixed registers per parity, so the compiler's wait counts let
-    // the loads of round u + 2 stay in flight across the store of round u + 1.
-    StageRegs ra, rb;   // round u lives in ra for even u, rb for odd u
-    int pid_e[NC], pid_o[NC];  // block-table entries for even / odd rounds
-    if (n_u > 0) {
-      int pid0[NC];
-      stage_pids(stage_of(0), pid0);
-      stage_pids(stage_of(1), pid_o);
-      stage_load(ra, pid0, live_of(0));
-      stage_pids(stage_of(2), pid_e);
-      stage_load(rb, pid_o, live_of(1));
-      stage_store(ra, stage_of(0), 0);
+    // Stage pipeline (in rounds).  Round u computes the group's stage of round u from
+    // buffer u % 2 while the copies of round u + 1 fly into the other buffer (left by round
+    // u - 1 before the last barrier); block-table entries run a round further ahead.
+    int pid_n[NC] = {};  // entries of the next round to copy
+    {
+      int pid0[NC] = {};
+      if (n_u > 0) stage_pids(stage_of(0), pid0);
+      // An explicit use of q before the first copy: the compiler (which does not count
+      // the copies) waits for q here, while the first block-table entries are in flight,
+      // and knows q has arrived on every path into the loop.
+      asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
+      int bad0 = 0;
+      if (live_of(0)) bad0 = stage_dma(0, pid0);
+      if (n_u > 0) stage_pids(stage_of(1), pid_n);
+      wait_copies();
+      if (live_of(0)) stage_fix(stage_of(0), 0, bad0);
     }
-    // An explicit use of q here, after the prologue has waited for younger loads: the
-    // compiler's wait counts then know q has arrived on every path into the loop, instead
-    // of waiting for it (and every load issued after it) at the top of each trip.
-    asm volatile("" ::"v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
     __syncthreads();
-    auto iteration = [&](int u, auto parity) __attribute__((always_inline)) {
-      constexpr int P = decltype(parity)::value;
-      const int buf = u & 1;
-      if constexpr (P == 0) {
-        stage_pids(stage_of(u + 3), pid_o);
-        stage_load(ra, pid_e, live_of(u + 2));
-      } else {
-        stage_pids(stage_of(u + 3), pid_e);
-        stage_load(rb, pid_o, live_of(u + 2));
-      }
-      if (live_of(u)) compute_stage_fast(buf, stage_of(u) * kStage);
-      // Stored on every round, also past the last one (the other buffer is not read
-      // again then): a store skipped on some paths would leave its loads pending at the
-      // loop back edge, and the compiler then waits for every load at the top of the loop.
-      if constexpr (P == 0)
-        stage_store(rb, stage_of(u + 1), buf ^ 1);
-      else
-        stage_store(ra, stage_of(u + 1), buf ^ 1);
+    for (int u = 0; u < n_u; ++u) {
+      int bad_n = 0;
+      if (live_of(u + 1)) bad_n = stage_dma((u + 1) & 1, pid_n);
+      stage_pids(stage_of(u + 2), pid_n);
+      if (live_of(u)) compute_stage_fast(u & 1, stage_of(u) * kStage);
+      wait_copies();
+      if (live_of(u + 1)) stage_fix(stage_of(u + 1), (u + 1) & 1, bad_n);
       __syncthreads();
-    };
-    int u = 0;
-    for (; u + 1 < n_u; u += 2) {
-      iteration(u, std::integral_constant<int, 0>{});
-      iteration(u + 1, std::integral_constant<int, 1>{});
     }
-    if (u < n_u && live_of(u)) compute_stage_fast(u & 1, stage_of(u) * kStage);
   }
 
   if constexpr (G > 1) {
