@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     int n_tokens, int num_q_heads, int num_kv_heads, int num_pages, double log2_theta,
     const float* __restrict__ inv_freq) {
   constexpr int GS = BS / kRows;  // blocks per page
-  __shared__ int cu_sh[kFastSeqs + 1], ctx_sh[kFastSeqs], nb_sh[256];
+  __shared__ int cu_sh[kFastSeqs + 1], ctx_sh[kFastSeqs], nb_sh[256], wsum_sh[4], cnt_sh[4];
   __shared__ int tok_sh[kRows], page_sh[kRows], slot_sh[kRows], pos_sh[kRows];
   __shared__ float cos_sh[ROPE ? kRows : 1][kHeadDim / 2], sin_sh[ROPE ? kRows : 1][kHeadDim / 2];
   extern __shared__ __attribute__((aligned(16))) uint16_t v_sh[];  // [kRows][Hkv][64]
@@ -107,21 +107,26 @@ __global__ __launch_bounds__(256) void append_kernel(
         nb = max(j1 - j0, 0);
       }
     }
-    nb_sh[tid] = nb;
+    // inclusive scan of the block counts: inside each wave by lane shuffles, then the
+    // totals of the lower waves added
+    const int wv = tid >> 6;
+    int inc = nb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off, 64);
+      if ((tid & 63) >= off) inc += y;
+    }
+    if ((tid & 63) == 63) wsum_sh[wv] = inc;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
-      const int x = tid >= off ? nb_sh[tid - off] : 0;
-      __syncthreads();
-      nb_sh[tid] += x;
-      __syncthreads();
-    }
-    if (blk >= nb_sh[255]) return;  // uniform: the whole workgroup leaves
-    int lo = 0, hi = n_seqs - 1;  // first sequence whose inclusive count exceeds blk
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (nb_sh[mid] > blk) hi = mid; else lo = mid + 1;
-    }
-    const int s = lo;
+    for (int k = 0; k < wv; ++k) inc += wsum_sh[k];
+    if (blk >= wsum_sh[0] + wsum_sh[1] + wsum_sh[2] + wsum_sh[3]) return;  // uniform
+    nb_sh[tid] = inc;
+    // the block's sequence is the first whose inclusive count exceeds blk: the number of
+    // sequences whose count does not (the counts never decrease)
+    const unsigned long long le = __ballot(tid < n_seqs && inc <= blk);
+    if ((tid & 63) == 0) cnt_sh[wv] = __popcll(le);
+    __syncthreads();
+    const int s = cnt_sh[0] + cnt_sh[1] + cnt_sh[2] + cnt_sh[3];
     const int first = cu_sh[s], n_s = cu_sh[s + 1] - first, fp = ctx_sh[s] - n_s;
     const int j0 = (fp >= 0 ? fp / (8 * GS) : -((-fp + 8 * GS - 1) / (8 * GS))) * GS;
     const int j = j0 + blk - (s > 0 ? nb_sh[s - 1] : 0);
