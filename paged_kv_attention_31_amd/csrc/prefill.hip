@@ -388,11 +388,10 @@ void prefill_kernel(
                                                    __builtin_bit_cast(bf16x8_t, pb), o1, 0, 0, 0);
     }
   };
-  // Both halves run even when the second lies past kend: it is then fully masked
-  // (p = 0, no rescale) and adds nothing, and the straight-line order keeps the second
-  // half's S^T products in flight during the first half's softmax.  The K operands of
-  // the stage are read from LDS up front; each half's V operands just before its
-  // softmax (holding all of them would cost the third wave per SIMD its registers).
+  // The second half's softmax and P.V are skipped when it lies wholly past kend; its S^T
+  // products are issued with the first half's, so they are in flight during the first
+  // half's softmax.  All K and V operands of the stage are read from LDS up front (with the
+  // copies going straight to LDS there is room for them at three waves per SIMD).
   auto compute_stage_fast = [&](int buf, int k0) __attribute__((always_inline)) {
     KOps k0o, k1o;
     read_k(buf, 0, k0o);
@@ -400,15 +399,12 @@ void prefill_kernel(
     uint32_t p0[8], p1[8], unused[8];
     const f32x16_t s0 = qk(k0o);
     const f32x16_t s1 = qk(k1o);
-    {
-      VOps v0o;
-      read_v(buf, 0, v0o);
-      softmax(s0, k0, p0, unused, std::false_type{});
-      pv(v0o, p0);
-    }
+    VOps v0o, v1o;
+    read_v(buf, 0, v0o);
+    read_v(buf, 1, v1o);
+    softmax(s0, k0, p0, unused, std::false_type{});
+    pv(v0o, p0);
     if (__builtin_expect(k0 + 32 < kend, 1)) {  // else masked whole: nothing to add
-      VOps v1o;
-      read_v(buf, 1, v1o);
       softmax(s1, k0 + 32, p1, unused, std::false_type{});
       pv(v1o, p1);
     }
