@@ -431,8 +431,8 @@ void prefill_kernel(
 
   // Key groups: group grp takes the piece's stages grp, grp + G, grp + 2G, ... (round u
   // holds stage grp + G u of every group); every group runs the same number of rounds, so
-  // the workgroup barriers match, and a stage past the piece is loaded the cheap way and
-  // not computed.
+  // the workgroup barriers match, and a round past the group's last stage copies and
+  // computes nothing.
   const int n_u = (n_stages + G - 1) / G;
   auto stage_of = [&](int u) __attribute__((always_inline)) { return st0 + grp + G * u; };
   auto live_of = [&](int u) __attribute__((always_inline)) { return grp + G * u < n_stages; };
