@@ -1032,13 +1032,23 @@ def run_serve() -> dict:
             "ms_per_step": wall * 1e3 / steps}
 
 
-def cpu_baseline_serve(budget_s: float) -> dict:
-    """The oracle scheduler over the same request stream, with the oracle's attention
-    (fp64, contiguous K/V) for the rows of its decode steps, one layer, until the budget
-    is spent."""
+def _serve_task(ctxs) -> int:
+    """The oracle's attention for a block of decode rows of the serve stream (one layer)."""
     import oracle as O
+
+    q, k, v = _POOL["sq"], _POOL["sk"], _POOL["sv"]
+    n = 0
+    for ctx in ctxs:
+        O.attention(q, k[:ctx], v[:ctx], [ctx], 0.125)
+        n += ctx * KV_BYTES_PER_TOKEN
+    return n
+
+
+def cpu_baseline_serve(budget_s: float) -> dict:
+    """The oracle scheduler over the same request stream (sequential: each step depends on
+    the last), then the oracle's attention (fp64, contiguous K/V) for the rows of its decode
+    steps, one layer, spread over the process pool in blocks of rows."""
     from oracle import sched as S
-    from threadpoolctl import threadpool_limits
 
     prompts, news = serve_stream()
     max_blocks = -(-(1024 + 128 - 1) // SERVE_BS)
@@ -1046,34 +1056,33 @@ def cpu_baseline_serve(budget_s: float) -> dict:
                      S.Pool(int(SERVE_SLOTS * max_blocks * 1.1)))
     for rid, (p, m) in enumerate(zip(prompts, news)):
         sc.submit(rid, p, m)
+    steps = 0
+    ctxs = []
+    a = time.perf_counter()
+    while True:
+        plan = sc.step()
+        steps += 1
+        if plan.kind == S.IDLE and not sc.queue and not sc.active:
+            break
+        if plan.kind == S.DECODE:
+            ctxs.extend(int(ctx) for _, _, ctx, _, _ in plan.rows)
+    sched_s = time.perf_counter() - a
     rng = np.random.default_rng(5)
-    k = rng.standard_normal((1024 + 128, 8, 64))
-    v = rng.standard_normal((1024 + 128, 8, 64))
-    q = rng.standard_normal((1, 32, 64))
-    steps = rows = 0
-    sched_s = attn_s = 0.0
-    nbytes = 0
-    with threadpool_limits(limits=1):
-        while attn_s + sched_s < budget_s:
-            a = time.perf_counter()
-            plan = sc.step()
-            sched_s += time.perf_counter() - a
-            steps += 1
-            if plan.kind == S.IDLE and not sc.queue and not sc.active:
-                break
-            if plan.kind != S.DECODE:
-                continue
-            a = time.perf_counter()
-            for _, _, ctx, _, _ in plan.rows:
-                O.attention(q, k[:ctx], v[:ctx], [ctx], 0.125)
-                nbytes += ctx * KV_BYTES_PER_TOKEN
-                rows += 1
-            attn_s += time.perf_counter() - a
-    return {"value": nbytes / attn_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle scheduler over the first {steps} steps of the same stream "
-                      f"({sched_s * 1e6 / steps:.0f} us/step), fp64 oracle attention of the "
-                      f"{rows} rows of its decode steps, one layer ({nbytes / 1e9:.2f} GB of "
-                      f"KV) in {attn_s:.1f} s, 1 thread"}
+    _POOL.update(sk=rng.standard_normal((1024 + 128, 8, 64)),
+                 sv=rng.standard_normal((1024 + 128, 8, 64)),
+                 sq=rng.standard_normal((1, 32, 64)))
+    tasks = [ctxs[i:i + 64] for i in range(0, len(ctxs), 64)]
+    try:
+        nbytes, passes, dt, workers, aff = pool_passes(_serve_task, tasks, CPU_TARGET_S, budget_s)
+    finally:
+        _POOL.clear()
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": workers, "affinity_cpus": aff,
+            "kind": "oracle",
+            "sample": f"oracle scheduler over the whole stream ({steps} steps, "
+                      f"{sched_s * 1e6 / steps:.0f} us/step, sequential), then fp64 oracle "
+                      f"attention of the {len(ctxs)} rows of its decode steps, one layer, "
+                      f"{passes} pass(es) ({nbytes / 1e9:.2f} GB of KV) in {dt:.2f} s on "
+                      f"{workers} worker processes, 1 BLAS thread each"}
 
 
 def main_serve(args) -> int:
