@@ -259,6 +259,22 @@ def test_prefill_chunked_ragged(bs, causal):
     assert_close(out, ref, f"prefill bs={bs} causal={causal}")
 
 
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_long_cached_prefix(bs, causal):
+    # chunks behind long cached prefixes: a small grid of many stages per tile (the K/V
+    # copies and their patches run through 20+ rounds per key group and block-table
+    # entries far into the row), contexts that end inside a page, and a one-token chunk
+    case = W.custom_case([5000, 3001, 77], [200, 1, 77], kind="prefill", block_size=bs,
+                         seed=76 + bs)
+    _announce(f"prefill long cached prefix bs={bs} causal={causal}")
+    g = GpuCase(case)
+    out = g.prefill(causal=causal)
+    kp, vp = oracle_pools(case)
+    ref = oracle_prefill(case, kp, vp, causal=causal)
+    assert_close(out, ref, f"prefill long prefix bs={bs} causal={causal}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 5, 8])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_key_splits(splits, causal):
