@@ -288,7 +288,8 @@ int pa_residual_rmsnorm(const void* x, const void* residual_in, void* residual_o
   if (n_rows == 0) return PA_OK;
   if (!x || !gamma || !out) return PA_ERR_INVALID_ARG;
   return hip_status(pa::launch_residual_rmsnorm(x, residual_in, residual_out, gamma, out, n_rows,
-                                                hidden, eps, static_cast<hipStream_t>(stream)));
+                                                hidden, eps, compute_units(),
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int pa_silu_mul(const void* gate, const void* up, int64_t ld_in, void* out, int64_t ld_out,

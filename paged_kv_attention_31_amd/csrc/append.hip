@@ -23,6 +23,7 @@
 // Rotation: pair i is (x[i], x[i + 32]), angle pos * f_i with f_i = theta^(-2i/64) or a
 // caller-given table; the angle is formed and reduced modulo 2 pi in fp64, its cosine
 // and sine rounded to fp32, the rotation done in fp32 and rounded once to bf16.
+// The new rows of K, V and Q are read once, with nontemporal loads.
 #include "common.h"
 #include "launch.h"
 
@@ -174,7 +175,8 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int r = e / (hd / 8);
     vr[i] = u32x4_t{0u, 0u, 0u, 0u};
     if (e < n_vchunks && tok_sh[r] >= 0)
-      vr[i] = *reinterpret_cast<const u32x4_t*>(v_new + (size_t)tok_sh[r] * hd + 8 * (e - r * (hd / 8)));
+      vr[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(v_new + (size_t)tok_sh[r] * hd + 8 * (e - r * (hd / 8))));
   }
   u32x4_t ka = {0u, 0u, 0u, 0u}, kb = ka;
   if (tid < n_kjobs) {
@@ -182,8 +184,8 @@ __global__ __launch_bounds__(256) void append_kernel(
     job(tid, num_kv_heads, r, g, k);
     if (tok_sh[r] >= 0) {
       const size_t src = (size_t)tok_sh[r] * hd + g * kHeadDim + 8 * k;
-      ka = *reinterpret_cast<const u32x4_t*>(k_new + src);
-      kb = *reinterpret_cast<const u32x4_t*>(k_new + src + 32);
+      ka = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_new + src));
+      kb = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_new + src + 32));
     }
   }
   u32x4_t qa[ROPE ? kQBatch : 1], qb[ROPE ? kQBatch : 1];
@@ -196,8 +198,8 @@ __global__ __launch_bounds__(256) void append_kernel(
       job(u, num_q_heads, r, h, k);
       if (q_in && u < n_qjobs && tok_sh[r] >= 0) {
         const size_t src = (size_t)tok_sh[r] * qd + h * kHeadDim + 8 * k;
-        qa[i] = *reinterpret_cast<const u32x4_t*>(q_in + src);
-        qb[i] = *reinterpret_cast<const u32x4_t*>(q_in + src + 32);
+        qa[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(q_in + src));
+        qb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(q_in + src + 32));
       }
     }
   }
@@ -214,7 +216,8 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int r = e / (hd / 8);
     u32x4_t x = {0u, 0u, 0u, 0u};
     if (tok_sh[r] >= 0)
-      x = *reinterpret_cast<const u32x4_t*>(v_new + (size_t)tok_sh[r] * hd + 8 * (e - r * (hd / 8)));
+      x = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(v_new + (size_t)tok_sh[r] * hd + 8 * (e - r * (hd / 8))));
     *reinterpret_cast<u32x4_t*>(v_sh + 8 * e) = x;
   }
   if constexpr (ROPE) {
@@ -251,8 +254,8 @@ __global__ __launch_bounds__(256) void append_kernel(
     job(u, num_kv_heads, r, g, k);
     if (page_sh[r] < 0) continue;
     const size_t src = (size_t)tok_sh[r] * hd + g * kHeadDim + 8 * k;
-    put_k(r, g, k, *reinterpret_cast<const u32x4_t*>(k_new + src),
-          *reinterpret_cast<const u32x4_t*>(k_new + src + 32));
+    put_k(r, g, k, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_new + src)),
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k_new + src + 32)));
   }
 
   // ---- V: per (head, dim) page row ---------------------------------------------------
@@ -294,8 +297,8 @@ __global__ __launch_bounds__(256) void append_kernel(
         job(u, num_q_heads, r, h, k);
         if (tok_sh[r] < 0) continue;
         const size_t src = (size_t)tok_sh[r] * qd + h * kHeadDim + 8 * k;
-        u32x4_t a = *reinterpret_cast<const u32x4_t*>(q_in + src);
-        u32x4_t b = *reinterpret_cast<const u32x4_t*>(q_in + src + 32);
+        u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(q_in + src));
+        u32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(q_in + src + 32));
         rotate8(a, b, &cos_sh[r][8 * k], &sin_sh[r][8 * k]);
         *reinterpret_cast<u32x4_t*>(q_out + src) = a;
         *reinterpret_cast<u32x4_t*>(q_out + src + 32) = b;

@@ -45,7 +45,7 @@ int rmsnorm_max_hidden();
 int silu_max_width();
 hipError_t launch_residual_rmsnorm(const void* x, const void* residual_in, void* residual_out,
                                    const void* gamma, void* out, int n_rows, int hidden,
-                                   float eps, hipStream_t stream);
+                                   float eps, int compute_units, hipStream_t stream);
 hipError_t launch_silu_mul(const void* gate, const void* up, int64_t ld_in, void* out,
                            int64_t ld_out, int n_rows, int width, int compute_units,
                            hipStream_t stream);

@@ -7,13 +7,21 @@
 // into the normalisation and the activation into the product keeps each activation row
 // to one pass through memory ("Tiny-vLLM 实战：用 C++/CUDA 手写高性能 LLM 推理引擎", §算子融合).
 //
-// residual_rmsnorm: one wave per row, four rows per 256-thread workgroup.  A lane holds up
-// to NC 16-byte chunks of its row in registers (chunk lane + 64 i), so the row is read once
-// and all of its loads are in flight together: h = x + r (fp32, rounded to bf16 and stored
-// as the next residual), the sum of h^2 over the row (a DPP reduction inside the wave, no
-// barrier), out = h * 1/sqrt(mean + eps) * gamma rounded once to bf16.
+// residual_rmsnorm: a wave normalises whole rows, four waves per 256-thread workgroup.  A
+// lane holds up to NC 16-byte chunks of a row in registers (chunk lane + 64 i), so a row is
+// read once and all of its loads are in flight together: h = x + r (fp32, rounded to bf16
+// and stored as the next residual), the sum of h^2 over the row (a DPP reduction inside
+// the wave, no barrier), out = h * 1/sqrt(mean + eps) * gamma rounded once to bf16.  Rows
+// of up to 4096 go grid-stride over one workgroup per compute unit, the next row's loads
+// issued before the current row's arithmetic and stores, so reads and writes overlap in
+// every wave; wider rows fill the registers with one row, and a wave takes a single row.
+// Rows are reached through buffer descriptors sized to the row (empty past the last row):
+// every load and store is issued unconditionally, which keeps the compiler's memory wait
+// counts exact across the loop.
 // silu_mul: a workgroup per (row, group of 256 U chunks); all 2U loads of a thread are
 // issued before the first product: out = g / (1 + e^-g) * u in fp32.
+// Both kernels read their activations once, with nontemporal loads; their outputs are
+// stored as usual, for the kernel that reads them next.
 #include <algorithm>
 
 #include "common.h"
@@ -25,44 +33,56 @@ namespace {
 
 constexpr int kMaxNormChunks = 16;  // 16-byte chunks per lane: rows up to 64 * 16 * 8 = 8192
 
+constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3: raw (untyped) access
+constexpr int kNontemporal = 2;         // cache policy of a buffer access: nt (read once)
+
+// A descriptor over one row of n_bytes (0 past the last row): loads outside it return zeros
+// and stores outside it are dropped, so every lane issues every load and store.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint16_t* p, int n_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, n_bytes, kRsrcWord3);
+}
+
+// Rows of up to 4096 (8 chunks per lane) keep two rows in registers and prefetch.
+template <int NC>
+constexpr bool kNormPrefetch = NC <= 8;
+
 template <bool RES, int NC>
-__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* r_in, uint16_t* r_out,  // r may be in place
-    const uint16_t* __restrict__ gamma, uint16_t* __restrict__ out, int n_rows, int hidden,
-    float eps) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= n_rows) return;  // wave-uniform, and the kernel has no workgroup barrier
-  const int lane = threadIdx.x & 63;
-  const int chunks = hidden >> 3;
-  const size_t base = (size_t)row * hidden;
-  // gamma joins the first batch of loads for rows of up to 2048; wider rows load it after
-  // the reduction, to keep the register count (and the occupancy) in bounds
-  constexpr bool kEarlyGamma = NC <= 4;
-  u32x4_t h[NC], b[NC], gm[NC];
+struct NormRow {
+  u32x4_t h[NC], b[NC];
+};
+
+// Issues the loads of x and r of one row (chunk lane + 64 i of the row in h[i], b[i]).
+template <bool RES, int NC>
+__device__ __forceinline__ void norm_load(NormRow<RES, NC>& v, __amdgpu_buffer_rsrc_t rx,
+                                          __amdgpu_buffer_rsrc_t rr, int lane) {
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const int c = lane + 64 * i;
-    h[i] = b[i] = gm[i] = u32x4_t{0u, 0u, 0u, 0u};
-    if (c < chunks) {
-      h[i] = *reinterpret_cast<const u32x4_t*>(x + base + 8 * c);
-      if constexpr (RES) b[i] = *reinterpret_cast<const u32x4_t*>(r_in + base + 8 * c);
-      if constexpr (kEarlyGamma) gm[i] = *reinterpret_cast<const u32x4_t*>(gamma + 8 * c);
-    }
+    v.h[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (lane + 64 * i) * 16, 0, kNontemporal);
+    if constexpr (RES)
+      v.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rr, (lane + 64 * i) * 16, 0, kNontemporal);
   }
+}
+
+// h = x + r (stored as the next residual), then out = h / sqrt(mean(h^2) + eps) * gamma.
+// Chunks past the row end hold zeros and add nothing to the sum of squares.
+template <bool RES, int NC, bool kEarlyGamma>
+__device__ __forceinline__ void norm_store(NormRow<RES, NC>& v, u32x4_t (&gm)[NC],
+                                           __amdgpu_buffer_rsrc_t rg, __amdgpu_buffer_rsrc_t rro,
+                                           __amdgpu_buffer_rsrc_t ro, int lane, int hidden,
+                                           float eps) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= chunks) continue;
     if constexpr (RES) {
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        h[i][w] = pack_bf16x2(bf_lo(h[i][w]) + bf_lo(b[i][w]), bf_hi(h[i][w]) + bf_hi(b[i][w]));
-      *reinterpret_cast<u32x4_t*>(r_out + base + 8 * c) = h[i];
+        v.h[i][w] = pack_bf16x2(bf_lo(v.h[i][w]) + bf_lo(v.b[i][w]),
+                                bf_hi(v.h[i][w]) + bf_hi(v.b[i][w]));
+      __builtin_amdgcn_raw_buffer_store_b128(v.h[i], rro, (lane + 64 * i) * 16, 0, 0);
     }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float lo = bf_lo(h[i][w]), hi = bf_hi(h[i][w]);
+      const float lo = bf_lo(v.h[i][w]), hi = bf_hi(v.h[i][w]);
       ss = __builtin_fmaf(lo, lo, ss);
       ss = __builtin_fmaf(hi, hi, ss);
     }
@@ -70,15 +90,73 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
   const float inv = 1.f / sqrtf(wave_sum(ss) / (float)hidden + eps);
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
-    const int c = lane + 64 * i;
-    if (c >= chunks) continue;
-    if constexpr (!kEarlyGamma) gm[i] = *reinterpret_cast<const u32x4_t*>(gamma + 8 * c);
+    if constexpr (!kEarlyGamma)
+      gm[i] = __builtin_amdgcn_raw_buffer_load_b128(rg, (lane + 64 * i) * 16, 0, 0);
     u32x4_t o;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      o[w] = pack_bf16x2(bf_lo(h[i][w]) * inv * bf_lo(gm[i][w]),
-                         bf_hi(h[i][w]) * inv * bf_hi(gm[i][w]));
-    *reinterpret_cast<u32x4_t*>(out + base + 8 * c) = o;
+      o[w] = pack_bf16x2(bf_lo(v.h[i][w]) * inv * bf_lo(gm[i][w]),
+                         bf_hi(v.h[i][w]) * inv * bf_hi(gm[i][w]));
+    __builtin_amdgcn_raw_buffer_store_b128(o, ro, (lane + 64 * i) * 16, 0, 0);
+  }
+}
+
+template <bool RES, int NC>
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* r_in, uint16_t* r_out,  // r may be in place
+    const uint16_t* __restrict__ gamma, uint16_t* __restrict__ out, int n_rows, int hidden,
+    float eps) {
+  const int stride = gridDim.x * 4;  // waves in the grid
+  int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (row >= n_rows) return;  // wave-uniform, and the kernel has no workgroup barrier
+  const int lane = threadIdx.x & 63;
+  const int row_bytes = hidden * 2;
+  // gamma is loaded once per wave for rows of up to 2048; wider rows load it after each
+  // reduction, to keep the register count in bounds
+  constexpr bool kEarlyGamma = NC <= 4;
+  const __amdgpu_buffer_rsrc_t rg = row_rsrc(gamma, row_bytes);
+  u32x4_t gm[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+    gm[i] = kEarlyGamma ? __builtin_amdgcn_raw_buffer_load_b128(rg, (lane + 64 * i) * 16, 0, 0)
+                        : u32x4_t{0u, 0u, 0u, 0u};
+  // past the last row the descriptors are empty: loads return zeros, stores are dropped
+  auto load = [&](NormRow<RES, NC>& v, int r) {
+    const bool live = r < n_rows;
+    const size_t off = (size_t)(live ? r : 0) * hidden;
+    const int n = live ? row_bytes : 0;
+    norm_load<RES, NC>(v, row_rsrc(x + off, n), row_rsrc(RES ? r_in + off : x, n), lane);
+  };
+  auto store = [&](NormRow<RES, NC>& v, int r) {
+    const bool live = r < n_rows;
+    const size_t off = (size_t)(live ? r : 0) * hidden;
+    const int n = live ? row_bytes : 0;
+    norm_store<RES, NC, kEarlyGamma>(v, gm, rg, row_rsrc(RES ? r_out + off : out, n),
+                                     row_rsrc(out + off, n), lane, hidden, eps);
+  };
+  NormRow<RES, NC> va;
+  if constexpr (!kNormPrefetch<NC>) {  // a row fills the registers: one at a time
+    for (; row < n_rows; row += stride) {
+      load(va, row);
+      store(va, row);
+    }
+    return;
+  } else {
+    // Rows row, row + stride, ...: the loads of the next row go out before the arithmetic
+    // and the stores of this one, two register sets in turn.  A pass takes two rows with
+    // no branch between them (the second may lie past the end), so every load is used in
+    // the code that follows it and none is moved later.
+    NormRow<RES, NC> vb;
+    load(va, row);
+    do {
+      load(vb, row + stride);
+      __builtin_amdgcn_sched_barrier(0);
+      store(va, row);
+      load(va, row + 2 * stride);
+      __builtin_amdgcn_sched_barrier(0);
+      store(vb, row + stride);
+      row += 2 * stride;
+    } while (row < n_rows);
   }
 }
 
@@ -102,8 +180,8 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(
     const int c = c0 + 256 * j;
     gv[j] = uv[j] = u32x4_t{0u, 0u, 0u, 0u};
     if (c < cpr) {
-      gv[j] = *reinterpret_cast<const u32x4_t*>(g + 8 * c);
-      uv[j] = *reinterpret_cast<const u32x4_t*>(u + 8 * c);
+      gv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(g + 8 * c));
+      uv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(u + 8 * c));
     }
   }
 #pragma unroll
@@ -119,20 +197,29 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(
   }
 }
 
+template <bool RES, int NC>
+void launch_norm(const uint16_t* x, const uint16_t* ri, uint16_t* ro, const uint16_t* gm,
+                 uint16_t* o, int n_rows, int hidden, float eps, int compute_units,
+                 hipStream_t stream) {
+  // a wave per row; with prefetch, at most one workgroup (four row streams) per compute unit
+  int wgs = (n_rows + 3) / 4;
+  if (kNormPrefetch<NC>) wgs = std::min(wgs, std::max(compute_units, 1));
+  hipLaunchKernelGGL((residual_rmsnorm_kernel<RES, NC>), dim3(wgs), dim3(256), 0, stream, x, ri,
+                     ro, gm, o, n_rows, hidden, eps);
+}
+
 template <bool RES>
 void launch_norm_rows(const uint16_t* x, const uint16_t* ri, uint16_t* ro, const uint16_t* gm,
-                      uint16_t* o, int n_rows, int hidden, float eps, hipStream_t stream) {
-  const dim3 grid((n_rows + 3) / 4), block(256);
+                      uint16_t* o, int n_rows, int hidden, float eps, int compute_units,
+                      hipStream_t stream) {
   const int per_lane = (hidden / 8 + 63) / 64;
   if (per_lane <= 4)
-    hipLaunchKernelGGL((residual_rmsnorm_kernel<RES, 4>), grid, block, 0, stream, x, ri, ro, gm, o,
-                       n_rows, hidden, eps);
+    launch_norm<RES, 4>(x, ri, ro, gm, o, n_rows, hidden, eps, compute_units, stream);
   else if (per_lane <= 8)
-    hipLaunchKernelGGL((residual_rmsnorm_kernel<RES, 8>), grid, block, 0, stream, x, ri, ro, gm, o,
-                       n_rows, hidden, eps);
+    launch_norm<RES, 8>(x, ri, ro, gm, o, n_rows, hidden, eps, compute_units, stream);
   else
-    hipLaunchKernelGGL((residual_rmsnorm_kernel<RES, kMaxNormChunks>), grid, block, 0, stream, x,
-                       ri, ro, gm, o, n_rows, hidden, eps);
+    launch_norm<RES, kMaxNormChunks>(x, ri, ro, gm, o, n_rows, hidden, eps, compute_units,
+                                     stream);
 }
 
 }  // namespace
@@ -143,16 +230,16 @@ int silu_max_width() { return 1 << 24; }  // 8192 groups of 256 chunks on grid a
 
 hipError_t launch_residual_rmsnorm(const void* x, const void* residual_in, void* residual_out,
                                    const void* gamma, void* out, int n_rows, int hidden,
-                                   float eps, hipStream_t stream) {
+                                   float eps, int compute_units, hipStream_t stream) {
   auto* xi = static_cast<const uint16_t*>(x);
   auto* ri = static_cast<const uint16_t*>(residual_in);
   auto* ro = static_cast<uint16_t*>(residual_out);
   auto* gm = static_cast<const uint16_t*>(gamma);
   auto* o = static_cast<uint16_t*>(out);
   if (residual_in)
-    launch_norm_rows<true>(xi, ri, ro, gm, o, n_rows, hidden, eps, stream);
+    launch_norm_rows<true>(xi, ri, ro, gm, o, n_rows, hidden, eps, compute_units, stream);
   else
-    launch_norm_rows<false>(xi, ri, ro, gm, o, n_rows, hidden, eps, stream);
+    launch_norm_rows<false>(xi, ri, ro, gm, o, n_rows, hidden, eps, compute_units, stream);
   return hipGetLastError();
 }
 

@@ -36,9 +36,13 @@ def _within_one_ulp(got, want, frac, what):
 
 # (4622, 2048): the 1B shape; the others reach every register budget of the kernel (rows
 # of up to 4, 8 and 16 chunks per lane), ragged chunk counts and row counts that leave a
-# workgroup part empty
+# workgroup part empty.  Above 1024 rows (four row streams per compute unit on 256 compute
+# units) a wave takes several rows, two per pass with the second maybe past the end: one to
+# nine rows a wave, odd and even counts, full and ragged rows, with and without prefetch.
 @pytest.mark.parametrize("rows,hidden", [(4622, 2048), (37, 8), (5, 136), (3, 8192),
-                                         (66, 2056), (9, 4096), (130, 6144)])
+                                         (66, 2056), (9, 4096), (130, 6144), (2500, 4096),
+                                         (3001, 3000), (2071, 1032), (9000, 2048),
+                                         (1100, 8192)])
 @pytest.mark.parametrize("with_res", [True, False])
 def test_residual_rmsnorm(rows, hidden, with_res):
     import torch
