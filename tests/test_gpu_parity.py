@@ -230,6 +230,25 @@ def test_decode_long_context_workload():
     _announce(f"cfg4: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
+@pytest.mark.parametrize("bs", [16, 32])
+def test_decode_one_very_long_sequence(bs):
+    """One 131072-token sequence beside a 5-token one, automatic partition: each of the long
+    sequence's 8 segments (2048 tiles) is cut over about 128 workers, so the merge combines
+    that many partials per row; every head of both sequences against the oracle."""
+    ctx = [131072, 5]
+    case = W.custom_case(ctx, [1, 1], block_size=bs, seed=130 + bs)
+    _announce(f"decode 1 x 131072 + 1 x 5, bs={bs}")
+    g = GpuCase(case)
+    out = g.decode()
+    refs = []
+    for s, n in enumerate(ctx):
+        kl, vl = case.logical_kv(s)
+        refs.append(O.attention(O.bf16_to_f64(case.q_decode[s:s + 1]), O.bf16_to_f64(kl),
+                                O.bf16_to_f64(vl), [n], case.scale))
+    mx, mean = assert_close(out, np.concatenate(refs), f"1 x 131072, bs {bs}")
+    _announce(f"1 x 131072 bs={bs}: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
 # ---------------------------------------------------------------------------------------
 # prefill
 # ---------------------------------------------------------------------------------------
