@@ -263,6 +263,22 @@ def test_prefill_workload_parity():
     _announce(f"prefill workload 3: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
+def test_prefill_chunk_behind_30k_prefix():
+    """A 256-token chunk behind a 29,744-token cached prefix (about 470 key stages per
+    tile) beside a short prompt, block size 32: the automatic plan (four key groups per
+    workgroup, each taking every fourth stage) and eight key pieces with their merge, both
+    against the oracle."""
+    case = W.custom_case([30000, 1200], [256, 37], kind="prefill", block_size=32, seed=140)
+    _announce("prefill chunk behind a 30k prefix")
+    g = GpuCase(case)
+    kp, vp = oracle_pools(case)
+    ref = oracle_prefill(case, kp, vp)
+    for splits in (0, 8):
+        out = g.prefill(kv_splits=splits)
+        mx, mean = assert_close(out, ref, f"30k prefix, kv_splits {splits}")
+        _announce(f"30k prefix kv_splits={splits}: max-abs {mx:.2e} mean-abs {mean:.2e}")
+
+
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_chunked_ragged(bs, causal):
