@@ -1,7 +1,7 @@
 """Pools past 4 GiB (marked ``gpu``): the same batches with every page id moved up far
 enough that the used pages sit more than 5 GiB into each pool must give, bit for bit, the
 outputs and page contents of the batches at the bottom of the pools, through pa_kv_append,
-pa_decode, pa_prefill, pa_decode_append and pa_copy_pages.  A page's content and the order
+pa_decode, pa_prefill, pa_rope_kv_append, pa_decode_append and pa_copy_pages.  A page's content and the order
 of every computation do not depend on its id, so any difference is a page address formed in
 32 bits somewhere."""
 
@@ -106,4 +106,36 @@ def test_decode_append_and_copy_past_4gib():
     for s_, d_ in zip(src.tolist(), dst.tolist()):
         assert _same(kp_hi[d_], kp_hi[s_]) and _same(vp_hi[d_], vp_hi[s_])
     del kp_lo, vp_lo, kp_hi, vp_hi, out_lo, out_hi
+    _free()
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_rope_append_past_4gib(bs):
+    import torch
+
+    import paged_kv_attention_31_amd as pa
+
+    case = W.custom_case([700, 129, 1024], [700, 1, 300], kind="prefill", block_size=bs,
+                         seed=128 + bs)
+    off = _lift_pages(case)
+    hq, hkv, d = case.num_q_heads, case.num_kv_heads, case.head_dim
+    t = int(case.cu_new_lens[-1])
+    _announce(f"rope_kv_append bs={bs}: page ids lifted by {off}")
+    q = bf16_dev(W.normal_bf16([77, 128 + bs], t * hq * d).reshape(t, hq, d))
+
+    def run(c: W.Case):
+        geom = geometry(c)
+        kp, vp = sentinel_pools(c)
+        q_out = torch.empty_like(q)
+        pa.rope_kv_append(geom, q, q_out, bf16_dev(c.k_new.reshape(t, hkv, d)),
+                          bf16_dev(c.v_new.reshape(t, hkv, d)), kp, vp, i32_dev(c.block_tables),
+                          i32_dev(c.cu_new_lens), i32_dev(c.ctx_lens))
+        return kp, vp, q_out
+
+    kp_lo, vp_lo, q_lo = run(case)
+    kp_hi, vp_hi, q_hi = run(_lifted(case, off))
+    torch.cuda.synchronize()
+    assert _same(q_hi, q_lo)
+    assert _same(kp_hi[off:], kp_lo) and _same(vp_hi[off:], vp_lo)
+    del kp_lo, vp_lo, kp_hi, vp_hi, q_lo, q_hi, q
     _free()
