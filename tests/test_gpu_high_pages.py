@@ -1,9 +1,9 @@
 """Pools past 4 GiB (marked ``gpu``): the same batches with every page id moved up far
 enough that the used pages sit more than 5 GiB into each pool must give, bit for bit, the
 outputs and page contents of the batches at the bottom of the pools, through pa_kv_append,
-pa_decode, pa_prefill, pa_rope_kv_append, pa_decode_append and pa_copy_pages.  A page's content and the order
-of every computation do not depend on its id, so any difference is a page address formed in
-32 bits somewhere."""
+pa_decode, pa_prefill, pa_rope_kv_append, pa_decode_append and pa_copy_pages.  A page's
+content and the order of every computation do not depend on its id, so any difference is a
+page address formed in 32 bits somewhere."""
 
 from __future__ import annotations
 
