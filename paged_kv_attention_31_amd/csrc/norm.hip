@@ -106,9 +106,10 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* r_in, uint16_t* r_out,  // r may be in place
     const uint16_t* __restrict__ gamma, uint16_t* __restrict__ out, int n_rows, int hidden,
     float eps) {
-  const int stride = gridDim.x * 4;  // waves in the grid
-  int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  if (row >= n_rows) return;  // wave-uniform, and the kernel has no workgroup barrier
+  const int64_t stride = (int64_t)gridDim.x * 4;  // waves in the grid
+  const int row0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (row0 >= n_rows) return;  // wave-uniform, and the kernel has no workgroup barrier
+  int64_t row = row0;  // 64-bit: the prefetch's rows past the last one never wrap around
   const int lane = threadIdx.x & 63;
   const int row_bytes = hidden * 2;
   // gamma is loaded once per wave for rows of up to 2048; wider rows load it after each
@@ -121,13 +122,13 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
     gm[i] = kEarlyGamma ? __builtin_amdgcn_raw_buffer_load_b128(rg, (lane + 64 * i) * 16, 0, 0)
                         : u32x4_t{0u, 0u, 0u, 0u};
   // past the last row the descriptors are empty: loads return zeros, stores are dropped
-  auto load = [&](NormRow<RES, NC>& v, int r) {
+  auto load = [&](NormRow<RES, NC>& v, int64_t r) {
     const bool live = r < n_rows;
     const size_t off = (size_t)(live ? r : 0) * hidden;
     const int n = live ? row_bytes : 0;
     norm_load<RES, NC>(v, row_rsrc(x + off, n), row_rsrc(RES ? r_in + off : x, n), lane);
   };
-  auto store = [&](NormRow<RES, NC>& v, int r) {
+  auto store = [&](NormRow<RES, NC>& v, int64_t r) {
     const bool live = r < n_rows;
     const size_t off = (size_t)(live ? r : 0) * hidden;
     const int n = live ? row_bytes : 0;
@@ -202,7 +203,7 @@ void launch_norm(const uint16_t* x, const uint16_t* ri, uint16_t* ro, const uint
                  uint16_t* o, int n_rows, int hidden, float eps, int compute_units,
                  hipStream_t stream) {
   // a wave per row; with prefetch, at most one workgroup (four row streams) per compute unit
-  int wgs = (n_rows + 3) / 4;
+  int wgs = n_rows / 4 + (n_rows % 4 != 0);
   if (kNormPrefetch<NC>) wgs = std::min(wgs, std::max(compute_units, 1));
   hipLaunchKernelGGL((residual_rmsnorm_kernel<RES, NC>), dim3(wgs), dim3(256), 0, stream, x, ri,
                      ro, gm, o, n_rows, hidden, eps);
