@@ -39,7 +39,7 @@ def _both_paths(case, part, ctx_override=None, bt_override=None):
     q = bf16_dev(case.q_decode)
     mc = int(max(int(ctx_h.max()), 1))
     ka, va, kb, vb = kp.clone(), vp.clone(), kp.clone(), vp.clone()
-    out_a = torch.empty((n, 32, 64), dtype=torch.bfloat16, device="cuda:0")
+    out_a = torch.empty((n, case.num_q_heads, d), dtype=torch.bfloat16, device="cuda:0")
     out_b = torch.empty_like(out_a)
     pa.kv_append(geom, k_new, v_new, ka, va, bt, i32_dev(np.arange(n + 1, dtype=np.int32)),
                  ctx)

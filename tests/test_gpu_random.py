@@ -2,8 +2,10 @@
 sequences, their lengths, decode or prefill, the decode partition, prefill causality and
 key pieces are drawn from a fixed seed.  The pools after the appends must equal the
 oracle's bit for bit, and every output row must meet the parity bar against the oracle.
-The draws cover combinations the hand-picked cases do not (other head counts with key
-pieces, empty contexts beside long ones, one-token chunks behind long prefixes)."""
+Decode batches without empty contexts also run pa_decode_append, which must give the same
+outputs and pools bit for bit.  The draws cover combinations the hand-picked cases do not
+(other head counts with key pieces, empty contexts beside long ones, one-token chunks behind
+long prefixes)."""
 
 from __future__ import annotations
 
@@ -13,6 +15,7 @@ import pytest
 import workloads as W
 from tests.gpu_helpers import GpuCase, assert_close, bits_host
 from tests.helpers import oracle_decode, oracle_pools, oracle_prefill
+from tests.test_gpu_decode_append import _both_paths
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +57,10 @@ def test_random_batch(i):
     if d["kind"] == "decode":
         out = g.decode(partition_tokens=d["part"])
         ref = oracle_decode(case, kp, vp)
+        if min(d["ctx"]) > 0:  # one new token per sequence: the fused call must match
+            a, b, same, _, _ = _both_paths(case, d["part"])
+            assert np.array_equal(a, b) and same, "pa_decode_append differs"
+            assert np.array_equal(a, bits_host(out))
     else:
         out = g.prefill(causal=d["causal"], kv_splits=d["splits"])
         ref = oracle_prefill(case, kp, vp, causal=d["causal"])
